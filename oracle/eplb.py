@@ -1,0 +1,148 @@
+"""Redundant experts and load-balanced placement (oracle side).
+
+Sources:
+* "6.4 Data parallelism and expert parallelism" (infra-guide), section 5.2: a
+  CPU simulation counts tokens per expert under power-law expert popularity
+  (seed 0, exponent 0.4, 256 experts, top-8, 4096 tokens) and compares the
+  busiest-rank / mean-rank load for contiguous placement, for placement by
+  observed load, and for placement with one redundant replica per rank.  The
+  balanced placement gives each redundant slot to the expert with the highest
+  load per replica, then places replicas heaviest first onto the currently
+  lightest rank that still has a free slot.  Section 5.3: with redundancy a
+  rank holds (experts + redundant) / EP physical experts.
+* "Expert Parallel and All-to-All Backends" (aiinfrainterviews), "Load
+  imbalance": redundant replicas split a hot expert's tokens.
+
+The skewed workload's rule for one rank (8 extra replicas for the 8 hottest
+local experts, tokens split round-robin) is ``hottest_replica_map``.
+"""
+from __future__ import annotations
+
+import bisect
+import itertools
+import random
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+
+# ---------------------------------------------------- one rank's replicas
+def hottest_replica_map(local_counts: Sequence[int], redundant: int):
+    """Map for one rank holding ``num_local`` logical experts plus
+    ``redundant`` extra physical experts: the ``redundant`` hottest local
+    experts (more local pairs first, lower id on ties) get one extra replica
+    each; physical id num_local + i is the second replica of the i-th hottest.
+
+    Returns (l2p [num_local, 2] int32 with -1 padding, rep_count [num_local]
+    int32, P)."""
+    counts = [int(c) for c in local_counts]
+    L = len(counts)
+    if not 0 <= redundant <= L:
+        raise ValueError("redundant must be in [0, num_local]")
+    max_rep = 2 if redundant > 0 else 1
+    l2p = np.full((L, max_rep), -1, dtype=np.int32)
+    l2p[:, 0] = np.arange(L, dtype=np.int32)
+    rep = np.ones(L, dtype=np.int32)
+    hottest = sorted(range(L), key=lambda e: (-counts[e], e))[:redundant]
+    for i, e in enumerate(hottest):
+        l2p[e, 1] = L + i
+        rep[e] = 2
+    return l2p, rep, L + redundant
+
+
+def replica_share(n: int, R: int) -> List[int]:
+    """Closed form of the round-robin split: replica r of an expert with n
+    pairs and R replicas receives ceil((n - r) / R) pairs."""
+    return [max(0, -(-(n - r) // R)) for r in range(R)]
+
+
+# ------------------------------------------------ the load simulation (5.2)
+def simulate_expert_counts(seed: int = 0, experts: int = 256, top_k: int = 8,
+                           tokens: int = 4096, skew: float = 0.4) -> List[int]:
+    """Token counts per expert under power-law popularity.
+
+    Expert i (before shuffling) has popularity 1/(i+1)^skew; the popularity
+    list is shuffled with Python's seeded Mersenne Twister; each token then
+    draws experts with probability proportional to popularity, one draw at a
+    time, until it holds ``top_k`` distinct ones.  A weighted draw is the
+    inverse-CDF lookup of one uniform variate in the cumulative popularity
+    (the same sampling ``random.choices`` performs)."""
+    rng = random.Random(seed)
+    pop = [1.0 / (i + 1) ** skew for i in range(experts)]
+    rng.shuffle(pop)
+    cum = list(itertools.accumulate(pop))
+    total = cum[-1] + 0.0
+    counts = [0] * experts
+    for _ in range(tokens):
+        picked = set()
+        while len(picked) < top_k:
+            picked.add(bisect.bisect(cum, rng.random() * total, 0,
+                                     experts - 1))
+        for e in picked:
+            counts[e] += 1
+    return counts
+
+
+def contiguous_load(counts: Sequence[int], ep: int) -> List[float]:
+    """Rank loads when rank g owns experts [g*E/ep, (g+1)*E/ep)."""
+    per = len(counts) // ep
+    return [float(sum(counts[g * per:(g + 1) * per])) for g in range(ep)]
+
+
+def plan_replicas(counts: Sequence[int], redundant: int) -> List[int]:
+    """Replica count per expert: each extra replica goes to the expert with
+    the highest load per replica at that moment (lower id on ties)."""
+    rep = [1] * len(counts)
+    for _ in range(redundant):
+        best = 0
+        for e in range(1, len(counts)):
+            if counts[e] * rep[best] > counts[best] * rep[e]:
+                best = e
+        rep[best] += 1
+    return rep
+
+
+def place_replicas(counts: Sequence[int], replicas: Sequence[int], ep: int
+                   ) -> Tuple[List[List[Tuple[int, int]]], List[float]]:
+    """Place every replica (load counts[e]/replicas[e]) heaviest first onto the
+    lightest rank with a free slot (lower rank on ties); each rank has
+    (total replicas) / ep slots.  Equal loads are taken in (expert, replica)
+    order.  Returns per rank the list of (expert, replica index) and the rank
+    loads."""
+    total = sum(replicas)
+    if total % ep:
+        raise ValueError("total replicas must divide evenly over the ranks")
+    slots = total // ep
+    copies = [(counts[e] / replicas[e], e, r)
+              for e in range(len(counts)) for r in range(replicas[e])]
+    copies.sort(key=lambda c: (-c[0], c[1], c[2]))
+    load = [0.0] * ep
+    held: List[List[Tuple[int, int]]] = [[] for _ in range(ep)]
+    for w, e, r in copies:
+        g = min((g for g in range(ep) if len(held[g]) < slots),
+                key=lambda g: (load[g], g))
+        load[g] += w
+        held[g].append((e, r))
+    return held, load
+
+
+def busiest_over_mean(load: Sequence[float]) -> float:
+    return max(load) / (sum(load) / len(load))
+
+
+def mean_over_busiest(load: Sequence[float]) -> float:
+    """The balancedness that vLLM's EPLB logs (mean / max, 1 is perfect)."""
+    return (sum(load) / len(load)) / max(load)
+
+
+def imbalance_table(counts: Sequence[int], eps=(8, 32, 64, 256)):
+    """busiest/mean per EP degree for contiguous placement, for placement by
+    load without redundancy, and with one redundant replica per rank."""
+    rows = []
+    for ep in eps:
+        c = busiest_over_mean(contiguous_load(counts, ep))
+        _, l0 = place_replicas(counts, plan_replicas(counts, 0), ep)
+        _, l1 = place_replicas(counts, plan_replicas(counts, ep), ep)
+        rows.append((ep, len(counts) // ep, c, busiest_over_mean(l0),
+                     busiest_over_mean(l1)))
+    return rows
