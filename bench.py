@@ -1,0 +1,268 @@
+"""Benchmark of the EP-rank MoE layer on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+One step = one moe_layer_forward (route -> dispatch -> grouped SwiGLU FFN ->
+combine) over one batch of synthetic input already resident in HBM.  The
+headline workload is the decode share of a GLM-5.3-shaped layer (T=256,
+H=6144, I=2048, 32 of 256 experts local, k=8, bf16).  Prints ONE JSON line.
+
+Besides throughput the line carries:
+* roofline: the dominant kernel's algorithmic bytes (or flops) per launch over
+  its average duration, timed with HIP events recorded by the library on the
+  layer's own stream (moe_layer_forward_timed), against MI355X's published
+  peak (HBM 8 TB/s; dense bf16 MFMA 2.5 PFLOP/s);
+* cpu_baseline: the float64 CPU oracle timed on this host on a bounded sample
+  of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s on 1 MI355X; decode HBM TB/s and prefill TFLOP/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """hipEvent plumbing through the HIP runtime's C API."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                               ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.h.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b) -> float:
+        assert self.h.hipEventSynchronize(b) == 0
+        t = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(t), a, b) == 0
+        return float(t.value)
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def kernel_units(wl, counts, P, phys_counts):
+    """Algorithmic work of the gate/up and down launches for this batch."""
+    H, I = wl.H, wl.I
+    wb = {"bf16": 2, "fp8": 1, "f32": 4}[wl.wdt]
+    ab = 1 if wl.wdt == "fp8" else (4 if wl.act == "f32" else 2)
+    hb = ab
+    nonempty = int(np.count_nonzero(phys_counts))
+    N = int(np.sum(phys_counts))
+    rows_sh = wl.T if wl.shared else 0
+    n_w = nonempty + (1 if wl.shared else 0)
+    rows = N + rows_sh
+    gu_bytes = n_w * 2 * H * I * wb + rows * H * ab + rows * I * hb
+    dn_bytes = n_w * I * H * wb + rows * I * hb + rows * H * 4
+    gu_flops = rows * 4.0 * H * I
+    dn_flops = rows * 2.0 * H * I
+    return dict(nonempty=nonempty, N=N, rows=rows, gu_bytes=gu_bytes,
+                dn_bytes=dn_bytes, gu_flops=gu_flops, dn_flops=dn_flops,
+                weight_bytes=n_w * 3 * H * I * wb)
+
+
+def cpu_baseline(wl, sample_tokens):
+    """The oracle as it stands, on the host cores, over a bounded sample."""
+    from oracle import moe as omoe
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    ex = omoe.expert_set_from_workload(wl, lazy=True)
+    res = omoe.layer_from_workload(wl, ex, token_subset=sample_tokens)
+    dt = time.perf_counter() - t0
+    n = len(sample_tokens)
+    return res, dict(value=n / dt, unit="tokens/s", cores=int(threads),
+                     kind="oracle",
+                     sample=f"{n} of {wl.T} tokens of the {wl.name} workload "
+                            f"(route + dispatch of all tokens, float64 experts "
+                            f"for the sampled ones), {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode",
+                    choices=["tiny", "decode", "prefill", "skewed", "fp8"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the CPU oracle baseline leg")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="oracle sample size (0 = workload default)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; "
+                          "--gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import expert_moe_fp32_amd as m
+    from expert_moe_fp32_amd import _lib as L
+    from expert_moe_fp32_amd.runner import DeviceLayer, to_dev
+    from synth import make_workload
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    wl = make_workload(args.workload, seed=args.seed)
+    log(f"bench: {wl.describe()}")
+    P = wl.num_local
+    prob = m.make_problem(T=wl.T, H=wl.H, I=wl.I, E=wl.E, k=wl.k,
+                          expert_begin=wl.expert_begin,
+                          num_local=wl.num_local, has_shared=wl.shared,
+                          act=wl.act, wdt=wl.wdt, out=wl.out)
+    t0 = time.perf_counter()
+    dl = DeviceLayer(prob, [wl.expert(e) for e in range(wl.num_local)],
+                     wl.shared_expert)
+    b = dl.buffers()
+    dlog, dx = to_dev(wl.logits), to_dev(wl.x)
+    dbias = None if wl.bias is None else to_dev(wl.bias)
+    torch.cuda.synchronize()
+    log(f"bench: inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = Hip()
+
+    def step():
+        dl.forward(b, dlog, dbias, dx)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # ---- timed region: exactly K layer forwards
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(e0, stream)
+    t_wall = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = hip.ms(e0, e1)
+    ms_per_step = total_ms / args.steps
+    log(f"bench: {args.steps} steps, {ms_per_step * 1e3:.1f} us/step "
+        f"(wall {wall * 1e3 / args.steps:.1f} us/step)")
+
+    # ---- per-stage durations, on the layer's stream
+    reps = max(10, min(args.steps, 50))
+    evs = [[hip.event() for _ in range(L.MOE_STAGE_EVENTS)] for _ in range(reps)]
+    for r in range(reps):
+        L.moe_layer_forward_timed(prob, dlog, dbias, dx, dl.weights, None,
+                                  None, b.out, b.counts, b.ws_layer,
+                                  b.ws_layer.numel(), evs[r], stream=stream)
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([hip.ms(evs[r][i], evs[r][i + 1])
+                                     for r in range(reps)]))
+                for i, name in enumerate(L.STAGES)}
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+
+    counts = b.counts.cpu().numpy()
+    off = b.offsets.cpu().numpy()[: P + 1]
+    phys_counts = np.diff(off)
+    u = kernel_units(wl, counts, P, phys_counts)
+    tokens_per_s = wl.T / (ms_per_step * 1e-3)
+    flops = u["gu_flops"] + u["dn_flops"]
+    layer_tflops = flops / (ms_per_step * 1e-3) / 1e12
+    weight_tbps = u["weight_bytes"] / (ms_per_step * 1e-3) / 1e12
+    # dominant kernel: the gate/up launch (2/3 of the weight bytes and flops)
+    gu_s = stage_ms["gate_up"] * 1e-3
+    dn_s = stage_ms["down"] * 1e-3
+    prec = "fp8" if wl.wdt == "fp8" else wl.act
+    ridge = MFMA_PEAK_TFLOPS[prec] * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    ai = u["gu_flops"] / u["gu_bytes"]
+    if ai < ridge:
+        achieved = u["gu_bytes"] / gu_s / 1e9
+        roof = dict(bound="hbm", kernel="gate_up", achieved=round(achieved, 1),
+                    peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
+                    algorithmic_bytes=int(u["gu_bytes"]),
+                    avg_us=round(gu_s * 1e6, 2))
+    else:
+        achieved = u["gu_flops"] / gu_s / 1e12
+        roof = dict(bound="mfma", kernel="gate_up", achieved=round(achieved, 1),
+                    peak=MFMA_PEAK_TFLOPS[prec], unit="TFLOP/s",
+                    frac=round(achieved / MFMA_PEAK_TFLOPS[prec], 4),
+                    traffic=None, algorithmic_flops=u["gu_flops"],
+                    avg_us=round(gu_s * 1e6, 2))
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prec,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I,
+                   "E": wl.E, "k": wl.k, "local_experts": wl.num_local,
+                   "shared_expert": wl.shared, "weights": wl.wdt,
+                   "activations": wl.act, "out": wl.out, "seed": wl.seed},
+        "roofline": roof,
+        "layer": {"weight_TBps": round(weight_tbps, 3),
+                  "weight_frac_of_hbm_peak": round(weight_tbps * 1e3 / HBM_PEAK_GBPS, 4),
+                  "TFLOPps": round(layer_tflops, 2),
+                  "mfma_frac": round(layer_tflops / MFMA_PEAK_TFLOPS[prec], 4),
+                  "local_rows": u["N"], "nonempty_experts": u["nonempty"],
+                  "expert_weight_bytes": u["weight_bytes"]},
+        "stages_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "down_GBps": round(u["dn_bytes"] / dn_s / 1e9, 1),
+    }
+    if not args.no_cpu:
+        n = args.cpu_tokens or {"tiny": 128, "decode": 256, "prefill": 16,
+                                "skewed": 16, "fp8": 16}[wl.name]
+        rng = np.random.default_rng(1)
+        tok = np.sort(rng.choice(wl.T, size=min(n, wl.T), replace=False))
+        log(f"bench: CPU oracle on {len(tok)} tokens ...")
+        res, base = cpu_baseline(wl, tok)
+        result["cpu_baseline"] = base
+        from oracle import moe as omoe
+        got = b.out[: wl.T * wl.H].cpu().numpy()
+        got = (omoe.bf16_to_f64(got.view(np.uint16)) if wl.out == "bf16"
+               else got.astype(np.float64)).reshape(wl.T, wl.H)[tok]
+        ref = res.out[tok]
+        rms = float(np.sqrt(np.mean(ref * ref)))
+        result["parity_sample_max_err_over_rms"] = float(
+            np.max(np.abs(got - ref)) / rms)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,13 @@
+"""Expert-parallel MoE layer on one EP rank's share, for MI355X (gfx950).
+
+The layer runs in the HIP library ``libmoe.so`` (C ABI in include/moe.h);
+``_lib`` is its ctypes binding and ``build`` compiles it with hipcc.
+"""
+from . import _lib  # noqa: F401
+from ._lib import (DeviceWeights, MoeError, Problem, Weights,  # noqa: F401
+                   device_weights, make_problem, moe_check_problem,
+                   moe_combine, moe_dispatch, moe_dispatch_workspace_size,
+                   moe_eplb_hottest_map, moe_ffn_workspace_size,
+                   moe_grouped_ffn, moe_layer_forward,
+                   moe_layer_workspace_size, moe_quantize_fp8_blocks,
+                   moe_route_topk, status_string)

@@ -1,0 +1,150 @@
+// Internal helpers shared by the HIP kernels of the MoE layer (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+typedef uint16_t bf16_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(8))) int32_t i32x8_t;
+
+#define MOE_WAVE 64
+#define MOE_KMAX 16          // largest k the dispatch kernels hold in registers
+#define MOE_EMAX 1024        // largest E the router handles (16 scores a lane)
+#define MOE_LMAX 1024        // largest num_local / num_physical
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// round-to-nearest-even float32 -> bf16 (finite values; NaN stays NaN)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (bf16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------- OCP E4M3
+// Round-to-nearest-even of a finite float32 to E4M3 ("e4m3fn": bias 7, no
+// infinities, S.1111.111 = NaN, max 448), saturating to +-448; sign copied.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {                 // |v| >= 448
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {           // |v| < 2^-6: subnormal range
+    // value = m * 2^-9 with m in [0, 8]; m = rne(|v| * 2^9)
+    float s = __uint_as_float(a) * 512.0f;  // exact scaling by a power of 2
+    uint32_t m = (uint32_t)__builtin_rintf(s);  // current rounding mode: RNE
+    code = m;                              // m == 8 is the smallest normal
+  } else {
+    // normal: keep 3 mantissa bits with RNE on the float32 bit pattern
+    uint32_t rounded = a + 0x7FFFFu + ((a >> 20) & 1u);
+    uint32_t e = (rounded >> 23) - 127 + 7;
+    uint32_t m = (rounded >> 20) & 7u;
+    code = (e << 3) | m;
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return (uint8_t)(sign | code);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
+  uint32_t s = (uint32_t)(c & 0x80u) << 24;
+  uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  float v;
+  if (e == 0) v = (float)m * 0.001953125f;  // m * 2^-9
+  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return __uint_as_float(__float_as_uint(v) | s);
+}
+
+static inline size_t moe_align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+static inline int moe_ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+// ------------------------------------------------------- launch functions
+namespace moe {
+
+hipError_t launch_route_topk(const float* logits, const float* bias, int T,
+                             int E, int k, int32_t* ids, float* w,
+                             int32_t* counts, hipStream_t s);
+
+struct DispatchArgs {
+  int T, k, expert_begin, num_local, P, max_rep, H;
+  const int32_t* ids;
+  const float* w;
+  const int32_t* l2p;       // may be null (identity)
+  const int32_t* rep;       // may be null
+  int32_t* block_counts;    // [nblk][L]
+  int32_t* block_base;      // [nblk][L]
+  int32_t* offsets;         // [P+1]
+  int32_t* row_token;
+  float* row_weight;
+  int32_t* pair_row;
+};
+int dispatch_blocks(int T);
+hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s);
+
+// x_perm[r] = x[row_token[r]] for r < offsets[P]; row_bytes % 16 == 0
+hipError_t launch_gather_rows(const void* x, size_t row_bytes,
+                              const int32_t* row_token,
+                              const int32_t* n_rows_dev, int cap, void* out,
+                              hipStream_t s);
+
+hipError_t launch_gather_rows_words(const void* x, int row_words,
+                                    const int32_t* row_token,
+                                    const int32_t* n_rows_dev, int cap,
+                                    void* out, hipStream_t s);
+
+// per-token per-128 E4M3 quantisation of bf16 rows [T][H]
+hipError_t launch_quant_rows_fp8(const bf16_t* x, int T, int H,
+                                 uint8_t* codes, float* scales, hipStream_t s);
+
+hipError_t launch_quant_blocks_fp8(const float* w, int rows, int cols,
+                                   uint8_t* codes, float* scales,
+                                   hipStream_t s);
+
+hipError_t launch_combine(const float* y_perm, const int32_t* pair_row,
+                          const float* w, const float* y_shared, int T, int H,
+                          int k, int out_dtype, void* out, hipStream_t s);
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
+
+// ------------------------------------------------------------- the FFN
+// One "group list" describes all the work of a grouped FFN call: the P
+// routed physical experts (rows from offsets) and optionally the shared
+// expert (group index P, rows 0..T-1 of its own input).
+struct FfnArgs {
+  int H, I, P, T, cap, has_shared;
+  int rows_hint;                      // expected rows per routed group
+  int act, wdt;                       // moe_dtype
+  const int32_t* offsets;             // [P+1] device
+  const void* a_routed;               // [cap][H]
+  const float* a_routed_scales;       // fp8: [cap][H/128]
+  const void* a_shared;               // [T][H]
+  const float* a_shared_scales;
+  const moe_weights* w;               // host copy of the struct
+  void* h;                            // [cap + T][I] intermediate
+  float* h_scales;                    // fp8: [cap + T][I/128]
+  float* y_routed;                    // [cap][H]
+  float* y_shared;                    // [T][H]
+  int4* tiles;                        // tile list scratch
+  int32_t* tile_count;                // [2] scratch
+  int max_tiles;
+  hipEvent_t* events;                 // optional: after tiles, gate/up, down
+};
+size_t ffn_scratch_bytes(int H, int I, int P, int T, int cap, int has_shared,
+                         int act, int wdt);
+hipError_t launch_ffn(FfnArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -185,27 +185,54 @@ class ExpertSet:
     """Expert weights in float64, as the layer consumes them.
 
     ``fmt`` is the activation/weight recipe: "f32", "bf16" or "fp8".  For fp8,
-    weights are the exact values of the block-quantised codes."""
+    weights are the exact values of the block-quantised codes.  Either
+    ``experts`` holds (wg, wu, wd) per local logical expert, or ``loader(e)``
+    produces them on demand (large workloads: one expert at a time)."""
     fmt: str
-    experts: List[tuple]            # per local logical expert: (wg, wu, wd)
+    experts: Optional[List[tuple]] = None
     shared: Optional[tuple] = None
     quant_block: int = 128
+    loader: Optional[object] = None
+    shared_loader: Optional[object] = None
+
+    def get(self, e: int) -> tuple:
+        if self.experts is not None:
+            return self.experts[e]
+        return self.loader(e)
+
+    def get_shared(self) -> Optional[tuple]:
+        if self.shared is not None or self.shared_loader is None:
+            return self.shared
+        return self.shared_loader()
+
+    @property
+    def has_shared(self) -> bool:
+        return self.shared is not None or self.shared_loader is not None
 
 
-def expert_set_from_workload(w, experts: Optional[Sequence[int]] = None
-                             ) -> ExpertSet:
+def expert_set_from_workload(w, experts: Optional[Sequence[int]] = None,
+                             lazy: bool = False) -> ExpertSet:
     """Convert a synthetic workload's stored weights to float64; fp8
-    workloads are block-quantised here, by the oracle's own quantiser."""
-    idx = range(w.num_local) if experts is None else experts
+    workloads are block-quantised here, by the oracle's own quantiser.  With
+    ``lazy`` nothing is converted until an expert is used."""
     conv = _weight_converter(w.wdt, w.quant_block)
+
+    def load(e):
+        d = w.expert(e)
+        return conv(d["wg"]), conv(d["wu"]), conv(d["wd"])
+
+    def load_shared():
+        d = w.shared_expert
+        return conv(d["wg"]), conv(d["wu"]), conv(d["wd"])
+
+    if lazy:
+        return ExpertSet(fmt=w.wdt, quant_block=w.quant_block, loader=load,
+                         shared_loader=load_shared if w.shared else None)
+    idx = range(w.num_local) if experts is None else experts
     ex = [None] * w.num_local
     for e in idx:
-        d = w.expert(e)
-        ex[e] = (conv(d["wg"]), conv(d["wu"]), conv(d["wd"]))
-    sh = None
-    if w.shared:
-        d = w.shared_expert
-        sh = (conv(d["wg"]), conv(d["wu"]), conv(d["wd"]))
+        ex[e] = load(e)
+    sh = load_shared() if w.shared else None
     return ExpertSet(fmt=w.wdt, experts=ex, shared=sh,
                      quant_block=w.quant_block)
 
@@ -299,6 +326,7 @@ def layer_forward(logits, bias, x_stored, act: str, k: int, expert_begin: int,
         want = np.zeros(T, dtype=bool)
         want[np.asarray(token_subset)] = True
     y_rows = np.zeros((d.N, H), dtype=np.float64)
+    by_expert = {}
     for p in range(P):
         lo, hi = int(d.offsets[p]), int(d.offsets[p + 1])
         if hi == lo:
@@ -307,12 +335,16 @@ def layer_forward(logits, bias, x_stored, act: str, k: int, expert_begin: int,
         rows = rows[want[d.row_token[rows]]]
         if rows.size == 0:
             continue
-        wg, wu, wd = experts.experts[phys_to_logical[p]]
-        y_rows[rows] = swiglu(x_rows[d.row_token[rows]], wg, wu, wd, hr)
+        by_expert.setdefault(int(phys_to_logical[p]), []).append(rows)
+    for e, parts in sorted(by_expert.items()):
+        wg, wu, wd = experts.get(e)
+        for rows in parts:
+            y_rows[rows] = swiglu(x_rows[d.row_token[rows]], wg, wu, wd, hr)
+        del wg, wu, wd
     shared_out = None
-    if experts.shared is not None:
+    if experts.has_shared:
         shared_out = np.zeros((T, H), dtype=np.float64)
-        wg, wu, wd = experts.shared
+        wg, wu, wd = experts.get_shared()
         shared_out[want] = swiglu(x_rows[want], wg, wu, wd, hr)
     pr = d.pair_row.copy()
     pr[~want] = -1
@@ -370,11 +402,11 @@ def dense_masked_forward(logits, bias, x_stored, act: str, k: int,
             gate[t, e] = p[e] / tot
     out = np.zeros((T, H), dtype=np.float64)
     for e_loc in range(num_local):
-        wg, wu, wd = experts.experts[e_loc]
+        wg, wu, wd = experts.get(e_loc)
         y_all = swiglu(x_rows, wg, wu, wd, hr)
         out += gate[:, expert_begin + e_loc][:, None] * y_all
-    if experts.shared is not None:
-        wg, wu, wd = experts.shared
+    if experts.has_shared:
+        wg, wu, wd = experts.get_shared()
         out += swiglu(x_rows, wg, wu, wd, hr)
     return out
 
