@@ -172,7 +172,7 @@ def main():
     total_ms = hip.ms(e0, e1)
     ms_per_step = total_ms / args.steps
     log(f"bench: {args.steps} steps, {ms_per_step * 1e3:.1f} us/step "
-        f"(wall {wall * 1e3 / args.steps:.1f} us/step)")
+        f"(wall {wall * 1e6 / args.steps:.1f} us/step)")
 
     # ---- per-stage durations, on the layer's stream
     reps = max(10, min(args.steps, 50))
@@ -190,8 +190,8 @@ def main():
             hip.destroy(e)
 
     counts = b.counts.cpu().numpy()
-    off = b.offsets.cpu().numpy()[: P + 1]
-    phys_counts = np.diff(off)
+    # identity replica map: physical expert e is local logical expert e
+    phys_counts = counts[wl.expert_begin: wl.expert_begin + wl.num_local]
     u = kernel_units(wl, counts, P, phys_counts)
     tokens_per_s = wl.T / (ms_per_step * 1e-3)
     flops = u["gu_flops"] + u["dn_flops"]

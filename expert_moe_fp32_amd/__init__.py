@@ -10,4 +10,4 @@ from ._lib import (DeviceWeights, MoeError, Problem, Weights,  # noqa: F401
                    moe_eplb_hottest_map, moe_ffn_workspace_size,
                    moe_grouped_ffn, moe_layer_forward,
                    moe_layer_workspace_size, moe_quantize_fp8_blocks,
-                   moe_route_topk, status_string)
+                   moe_prepack_weights, moe_route_topk, status_string)

@@ -25,7 +25,8 @@ EXPORTS = (
     "moe_status_string", "moe_check_problem", "moe_dispatch_workspace_size",
     "moe_ffn_workspace_size", "moe_layer_workspace_size", "moe_route_topk",
     "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-    "moe_layer_forward_timed", "moe_quantize_fp8_blocks",
+    "moe_layer_forward_timed", "moe_prepack_weights",
+    "moe_quantize_fp8_blocks",
     "moe_eplb_hottest_map",
 )
 MOE_STAGE_EVENTS = 8
@@ -86,6 +87,7 @@ def lib() -> ctypes.CDLL:
                                                        ctypes.POINTER(Weights),
                                                        V, V, V, V, V, S, V,
                                                        V]),
+            "moe_prepack_weights": (ctypes.c_int, [V, I32, I32, I32, V, V]),
             "moe_quantize_fp8_blocks": (ctypes.c_int, [V, I32, I32, I32, V, V,
                                                        V]),
             "moe_eplb_hottest_map": (ctypes.c_int, [V, I32, I32, V, V, V]),
@@ -229,6 +231,16 @@ def moe_layer_forward_timed(p, logits, bias, x, weights: Weights, l2p,
         ctypes.addressof(ev))
     if check:
         _check(st, "moe_layer_forward_timed")
+    return st
+
+
+def moe_prepack_weights(src, rows, cols, dtype, dst, stream=None,
+                        check=True) -> int:
+    st = lib().moe_prepack_weights(
+        ptr(src), rows, cols, dtype, ptr(dst),
+        stream if stream is not None else current_stream())
+    if check:
+        _check(st, "moe_prepack_weights")
     return st
 
 

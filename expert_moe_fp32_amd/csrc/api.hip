@@ -95,8 +95,10 @@ moe_status launch_ffn_common(const moe_problem* p, const void* x_perm,
                              const float* x_shared_scales,
                              const moe_weights* w, float* y_perm,
                              float* y_shared, const FfnScratch& fs,
-                             hipStream_t s, hipEvent_t* events = nullptr) {
+                             hipStream_t s, hipEvent_t* events = nullptr,
+                             const int32_t* a_rows = nullptr) {
   FfnArgs a{};
+  a.a_rows = a_rows;
   a.H = p->H;
   a.I = p->I;
   a.P = p->num_physical;
@@ -143,7 +145,8 @@ moe_status dispatch_impl(const moe_problem* p, const void* x,
                          void* x_perm, float* x_perm_scales, int32_t* offsets,
                          int32_t* row_token, float* row_weight,
                          int32_t* pair_row, const DispatchScratch& d,
-                         hipStream_t s, hipEvent_t ev_index = nullptr) {
+                         hipStream_t s, hipEvent_t ev_index = nullptr,
+                         bool materialize = true) {
   DispatchArgs a{};
   a.T = p->T;
   a.k = p->k;
@@ -169,7 +172,7 @@ moe_status dispatch_impl(const moe_problem* p, const void* x,
   const int32_t* nrows = offsets + p->num_physical;
   if (p->weight_dtype == MOE_FP8_E4M3) {
     e = launch_quant_rows_fp8((const bf16_t*)x, p->T, p->H, d.xq, d.xs, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (e != hipSuccess || !materialize) return hip_status(e);
     e = launch_gather_rows(d.xq, (size_t)p->H, row_token, nrows, cap, x_perm, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     // scales: H/128 floats per row, gathered 4 bytes at a time
@@ -177,6 +180,7 @@ moe_status dispatch_impl(const moe_problem* p, const void* x,
                                  x_perm_scales, s);
     return hip_status(e);
   }
+  if (!materialize) return MOE_OK;
   e = launch_gather_rows(x, (size_t)p->H * dtype_bytes(p->act_dtype),
                          row_token, nrows, cap, x_perm, s);
   return hip_status(e);
@@ -274,9 +278,7 @@ LayerScratch carve_layer(Carver& c, const moe_problem* p) {
   L.row_token = c.take<int32_t>(cap);
   L.row_weight = c.take<float>(cap);
   L.pair_row = c.take<int32_t>(Tk);
-  const bool fp8 = p->weight_dtype == MOE_FP8_E4M3;
-  L.x_perm = c.take<char>(cap * p->H * (fp8 ? 1 : dtype_bytes(p->act_dtype)));
-  if (fp8) L.x_perm_scales = c.take<float>(cap * (p->H / 128));
+  // no permuted activation copy: the expert kernels gather rows themselves
   L.y_perm = c.take<float>(cap * p->H);
   if (p->has_shared) L.y_shared = c.take<float>((size_t)p->T * p->H);
   L.d = carve_dispatch(c, p);
@@ -413,15 +415,20 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
   if (ev) hipEventRecord(ev[1], s);
   st = dispatch_impl(p, x, L.ids, L.tw, l2p, replica_count, L.x_perm,
                      L.x_perm_scales, L.offsets, L.row_token, L.row_weight,
-                     L.pair_row, L.d, s, ev ? ev[2] : nullptr);
+                     L.pair_row, L.d, s, ev ? ev[2] : nullptr,
+                     /*materialize=*/false);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[3], s);
+  // The expert kernels read each routed row straight from the token rows
+  // through row_token (the permuted copy is never written); the shared
+  // expert reads the same token rows in order.
   const bool fp8 = p->weight_dtype == MOE_FP8_E4M3;
   const void* xs = fp8 ? (const void*)L.d.xq : x;
-  st = launch_ffn_common(p, L.x_perm, L.x_perm_scales, L.offsets,
+  st = launch_ffn_common(p, xs, fp8 ? L.d.xs : nullptr, L.offsets,
                          p->has_shared ? xs : nullptr,
                          p->has_shared && fp8 ? L.d.xs : nullptr, w, L.y_perm,
-                         L.y_shared, L.f, s, ev ? ev + 4 : nullptr);
+                         L.y_shared, L.f, s, ev ? ev + 4 : nullptr,
+                         L.row_token);
   if (st != MOE_OK) return st;
   st = hip_status(launch_combine(L.y_perm, L.pair_row, L.tw,
                                  p->has_shared ? L.y_shared : nullptr, p->T,
@@ -455,6 +462,16 @@ moe_status moe_layer_forward_timed(const moe_problem* p, const float* logits,
   }
   return layer_impl(p, logits, bias, x, w, l2p, replica_count, out,
                     expert_counts, workspace, ws_bytes, stream, ev);
+}
+
+moe_status moe_prepack_weights(const void* src, int32_t rows, int32_t cols,
+                               int32_t dtype, void* dst, void* stream) {
+  if (rows < 0 || cols < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (rows % 16 || cols % 32) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!src || !dst || src == dst) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_pack_bf16((const bf16_t*)src, rows, cols, dst, S(stream)));
 }
 
 moe_status moe_quantize_fp8_blocks(const float* w, int32_t rows, int32_t cols,

@@ -129,7 +129,8 @@ struct FfnArgs {
   int rows_hint;                      // expected rows per routed group
   int act, wdt;                       // moe_dtype
   const int32_t* offsets;             // [P+1] device
-  const void* a_routed;               // [cap][H]
+  const void* a_routed;               // [cap][H], or [T][H] through a_rows
+  const int32_t* a_rows;              // row_token of each routed row, or null
   const float* a_routed_scales;       // fp8: [cap][H/128]
   const void* a_shared;               // [T][H]
   const float* a_shared_scales;
@@ -146,5 +147,9 @@ struct FfnArgs {
 size_t ffn_scratch_bytes(int H, int I, int P, int T, int cap, int has_shared,
                          int act, int wdt);
 hipError_t launch_ffn(FfnArgs& a, hipStream_t s);
+
+// natural output-major bf16 [R][C] -> packed 16x32 operand blocks
+hipError_t launch_pack_bf16(const bf16_t* src, int R, int C, void* dst,
+                            hipStream_t s);
 
 }  // namespace moe

@@ -9,22 +9,29 @@
 // many rows simply owns more tiles and spreads over all CUs, and an expert
 // with no rows owns none and its weights are never read.
 //
-// Two bf16 kernels share the tile list:
-//  * k_stream_bf16 (groups of a few rows, decode): weights go straight from
-//    HBM into MFMA operand registers, each lane loading 64 contiguous bytes
-//    of one output channel per 128-wide K chunk, one chunk ahead; every weight
-//    byte is read once per tile.
-//  * k_tile_bf16 (groups of hundreds of rows, prefill): 128-row x 128-column
-//    tiles staged through double-buffered LDS, 2x2 wavefronts of 64x64.
-// Both use v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the gate/up pass
-// ends in the fused epilogue h = silu(g) * u rounded to bf16, the down pass
-// writes y in float32.
+// bf16 weights arrive in the packed operand layout written by
+// moe_prepack_weights: a matrix stored output-major [R][C] (C = reduction) is
+// cut into 16 x 32 blocks, block (r/16, c/32) stored at block index
+// (r/16) * (C/32) + c/32, 1 KiB each, and inside a block lane
+// L = r%16 + 16 * ((c%32)/8) holds the 8 consecutive values c%8 = 0..7.  A
+// block is exactly one wavefront's operand of v_mfma_f32_16x16x32_bf16, so a
+// 16-B load per lane reads 1 KiB of contiguous memory, and 16 output
+// channels over the whole reduction are one contiguous run.
 //
-// MFMA operand convention: for one 16x16x32 step, lane l supplies row (or
-// column) l % 16 and the 8 K-values of K-slot l / 16.  The K-values a lane
-// carries are the same set for the A and the B operand, so the product sums
-// every K index exactly once whatever order the slots take; this lets a lane
-// read one contiguous run of K for several steps.  The accumulator of lane l
+// Two bf16 kernels share the tile list:
+//  * k_stream_bf16 (groups of a few rows, decode): each wavefront streams its
+//    16 output channels' contiguous run straight into MFMA operand registers
+//    with non-temporal loads, one 128-wide K chunk ahead; every weight byte
+//    is read once per tile.
+//  * k_tile_bf16 (groups of hundreds of rows, prefill): 128 rows x 128
+//    columns per workgroup, double-buffered LDS holding operand blocks in
+//    lane order (conflict-free 16-B reads, no padding), 2x2 wavefronts of
+//    64 x 64.
+// The gate/up pass ends in the fused epilogue h = silu(g) * u rounded to
+// bf16; the down pass writes y in float32.
+//
+// MFMA operand convention (16x16x32 bf16): lane l supplies row (A) or column
+// (B) l % 16 and the 8 K-values of K-slot l / 16; the accumulator of lane l
 // holds rows 4 * (l / 16) + i, i < 4, of column l % 16.
 #include "common.h"
 
@@ -38,7 +45,8 @@ struct KArgs {
   int nb_per_tile;            // column blocks per tile
   int K, N;                   // reduction and output width
   int P, cap;
-  const void* a_routed;       // [cap][K] rows of the routed groups
+  const void* a_routed;       // rows of the routed groups ([cap][K], or [T][K]
+  const int32_t* a_rows;      //   indexed through a_rows[r] when non-null)
   const void* a_shared;       // [T][K] rows of the shared expert
   const void* const* w0_arr;  // gate (or down) per physical expert
   const void* const* w1_arr;  // up per physical expert
@@ -87,7 +95,19 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  0, 0, 0);
 }
 
-// Epilogue helpers: store a 16x16 accumulator block (lane layout above).
+__device__ __forceinline__ u32x4_t load_nt(const u32x4_t* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+// Row of the A operand for tile row `row` of a group.
+__device__ __forceinline__ const bf16_t* a_row(const KArgs& a, bool sh,
+                                               int row) {
+  if (sh) return (const bf16_t*)a.a_shared + (size_t)row * a.K;
+  const int src = a.a_rows ? a.a_rows[row] : row;
+  return (const bf16_t*)a.a_routed + (size_t)src * a.K;
+}
+
+// Store a 16x16 accumulator block (lane layout above).
 template <int MODE>
 __device__ __forceinline__ void store_block(const KArgs& a, bool sh, int row0,
                                             int nrows, int rbase, int n,
@@ -108,35 +128,34 @@ __device__ __forceinline__ void store_block(const KArgs& a, bool sh, int row0,
 }
 
 // ---------------------------------------------- weight-streaming kernel
-// Workgroup = 4 wavefronts = 64 output columns; wavefront = 16 columns; a
-// tile has up to 16*NMB rows.  K chunk = 128 (4 MFMA steps); lane (c, q)
-// reads K range [k0 + 32q, k0 + 32q + 32) of its row / column.
+// Workgroup = 4 wavefronts = 64 output columns; wavefront w streams packed
+// row block nb*4 + w (16 channels) over the whole reduction; a tile has up to
+// 16*NMB rows.  K chunk = 128 (4 MFMA steps), prefetched one chunk ahead.
 template <int MODE, int NMB>
 __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c16 = lane & 15, q = lane >> 4;
   const int total = a.tile_count[0] * a.nb_per_tile;
-  const int K = a.K;
+  const int K = a.K, KB = K / 32;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int tile = item / a.nb_per_tile;
     const int nb = item - tile * a.nb_per_tile;
     const int4 td = a.tiles[tile];
     const int g = td.x, row0 = td.y, nrows = td.z;
     const bool sh = g == a.P;
-    const bf16_t* A = (const bf16_t*)(sh ? a.a_shared : a.a_routed);
-    const bf16_t* W0 = (const bf16_t*)(sh ? a.w0_sh : a.w0_arr[g]);
-    const bf16_t* W1 = nullptr;
-    if (MODE == MODE_GATEUP) W1 = (const bf16_t*)(sh ? a.w1_sh : a.w1_arr[g]);
-    const int n = nb * 64 + wv * 16 + c16;
-    const u32x4_t* b0p = (const u32x4_t*)(W0 + (size_t)n * K + 32 * q);
-    const u32x4_t* b1p = (const u32x4_t*)(W1 + (size_t)n * K + 32 * q);
-    const u32x4_t* ap[NMB];
+    const int nb16 = nb * 4 + wv;
+    const u32x4_t* b0p = (const u32x4_t*)(sh ? a.w0_sh : a.w0_arr[g]) +
+                         (size_t)nb16 * KB * 64 + lane;
+    const u32x4_t* b1p = b0p;
+    if (MODE == MODE_GATEUP)
+      b1p = (const u32x4_t*)(sh ? a.w1_sh : a.w1_arr[g]) + (size_t)nb16 * KB * 64 + lane;
+    const bf16_t* ap[NMB];
     bool av[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       const int r = mb * 16 + c16;
       av[mb] = r < nrows;
-      ap[mb] = (const u32x4_t*)(A + (size_t)(row0 + (av[mb] ? r : 0)) * K + 32 * q);
+      ap[mb] = a_row(a, sh, row0 + (av[mb] ? r : 0)) + 8 * q;
     }
     const int nmb = (nrows + 15) >> 4;   // active row blocks (uniform)
     f32x4_t acc0[NMB], acc1[NMB];
@@ -149,23 +168,24 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
     u32x4_t b0c[4], b1c[4], acur[NMB][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      b0c[s] = b0p[s];
-      if (MODE == MODE_GATEUP) b1c[s] = b1p[s];
+      b0c[s] = load_nt(b0p + s * 64);
+      if (MODE == MODE_GATEUP) b1c[s] = load_nt(b1p + s * 64);
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) acur[mb][s] = av[mb] ? ap[mb][s] : zero;
+      for (int mb = 0; mb < NMB; ++mb)
+        acur[mb][s] = av[mb] ? *(const u32x4_t*)(ap[mb] + 32 * s) : zero;
     }
     for (int k0 = 0; k0 < K; k0 += 128) {
       u32x4_t b0n[4], b1n[4], anext[NMB][4];
       const bool more = k0 + 128 < K;
       if (more) {
-        const int o = (k0 + 128) / 8;     // in u32x4 units
+        const int kb = (k0 + 128) / 32;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          b0n[s] = b0p[o + s];
-          if (MODE == MODE_GATEUP) b1n[s] = b1p[o + s];
+          b0n[s] = load_nt(b0p + (kb + s) * 64);
+          if (MODE == MODE_GATEUP) b1n[s] = load_nt(b1p + (kb + s) * 64);
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb)
-            anext[mb][s] = av[mb] ? ap[mb][o + s] : zero;
+            anext[mb][s] = av[mb] ? *(const u32x4_t*)(ap[mb] + k0 + 128 + 32 * s) : zero;
         }
       }
 #pragma unroll
@@ -188,6 +208,7 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
         }
       }
     }
+    const int n = nb16 * 16 + c16;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       if (mb < nmb) store_block<MODE>(a, sh, row0, nrows, mb * 16, n, acc0[mb], acc1[mb]);
@@ -195,21 +216,22 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
 }
 
 // ----------------------------------------------------- LDS-tiled kernel
-// Tile: BM = 128 rows x 128 B-columns (gate/up: 64 gate + 64 up channels of
-// the same 64 outputs; down: 128 outputs), BK = 64, double-buffered LDS with
-// rows padded to 72 elements (conflict-free 16-byte reads for 16 lanes).
+// Tile: 128 rows x 128 B-columns (gate/up: 64 gate + 64 up channels of the
+// same 64 outputs; down: 128 outputs), BK = 64 (two MFMA steps).  LDS holds,
+// per stage, the A operand as 8 row blocks x 2 steps and the B operand as
+// 8 column blocks x 2 steps, each a 1 KiB lane-ordered block, so every
+// fragment read is one conflict-free ds_read_b128 at lane * 16 bytes.
 // Wavefront (wm, wn) of a 2x2 grid owns 64 rows x 64 B-columns.
-static constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = 72;
+static constexpr int TBM = 128, TBK = 64;
 
 template <int MODE>
 __global__ __launch_bounds__(256) void k_tile_bf16(KArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds_a[2][TBM * TLD];
-  __shared__ __attribute__((aligned(16))) bf16_t lds_b[2][TBN * TLD];
+  __shared__ u32x4_t lds_a[2][16 * 64];
+  __shared__ u32x4_t lds_b[2][16 * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
-  const int c16 = lane & 15, q = lane >> 4;
-  const int K = a.K;
+  const int K = a.K, KB = K / 32;
   const int total = a.tile_count[0] * a.nb_per_tile;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -218,36 +240,35 @@ __global__ __launch_bounds__(256) void k_tile_bf16(KArgs a) {
     const int4 td = a.tiles[tile];
     const int g = td.x, row0 = td.y, nrows = td.z;
     const bool sh = g == a.P;
-    const bf16_t* A = (const bf16_t*)(sh ? a.a_shared : a.a_routed);
-    const bf16_t* W0 = (const bf16_t*)(sh ? a.w0_sh : a.w0_arr[g]);
-    const bf16_t* W1 = W0;
-    if (MODE == MODE_GATEUP) W1 = (const bf16_t*)(sh ? a.w1_sh : a.w1_arr[g]);
-    // global source of the 4 16-byte chunks this thread stages per operand:
-    // chunk c = tid + 256 j covers row c / 8, columns 8 (c % 8) .. + 8
-    const u32x4_t* ga[4];
+    // Staging: chunk c = tid + 256 j (j < 4) is block c/64 = 4j + wv,
+    // lane c%64.  A block b = (row block b/2, step b%2); B block b = (column
+    // block b/2, step b%2).
+    const bf16_t* ga[4];
     const u32x4_t* gb[4];
     bool va[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j;
-      const int r = c >> 3, col = (c & 7) * 8;
+      const int blk = 4 * j + wv;
+      const int r = (blk >> 1) * 16 + (lane & 15);
       va[j] = r < nrows;
-      ga[j] = (const u32x4_t*)(A + (size_t)(row0 + (va[j] ? r : 0)) * K + col);
-      int wrow;
-      const bf16_t* W;
-      if (MODE == MODE_GATEUP) {       // rows 0..63 gate, 64..127 up
-        W = r < 64 ? W0 : W1;
-        wrow = nb * 64 + (r & 63);
+      ga[j] = a_row(a, sh, row0 + (va[j] ? r : 0)) + (blk & 1) * 32 + (lane >> 4) * 8;
+      const int cb = blk >> 1;           // local column block 0..7
+      const u32x4_t* W;
+      int nb16;
+      if (MODE == MODE_GATEUP) {         // blocks 0..3 gate, 4..7 up
+        W = (const u32x4_t*)(cb < 4 ? (sh ? a.w0_sh : a.w0_arr[g])
+                                    : (sh ? a.w1_sh : a.w1_arr[g]));
+        nb16 = nb * 4 + (cb & 3);
       } else {
-        W = W0;
-        wrow = nb * 128 + r;
+        W = (const u32x4_t*)(sh ? a.w0_sh : a.w0_arr[g]);
+        nb16 = nb * 8 + cb;
       }
-      gb[j] = (const u32x4_t*)(W + (size_t)wrow * K + col);
+      gb[j] = W + ((size_t)nb16 * KB + (blk & 1)) * 64 + lane;
     }
     u32x4_t ra[4], rb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      ra[j] = va[j] ? ga[j][0] : zero;
+      ra[j] = va[j] ? *(const u32x4_t*)ga[j] : zero;
       rb[j] = gb[j][0];
     }
     f32x4_t acc[4][4];
@@ -259,9 +280,8 @@ __global__ __launch_bounds__(256) void k_tile_bf16(KArgs a) {
     __syncthreads();   // the previous item's readers are done with LDS
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j;
-      *(u32x4_t*)&lds_a[0][(c >> 3) * TLD + (c & 7) * 8] = ra[j];
-      *(u32x4_t*)&lds_b[0][(c >> 3) * TLD + (c & 7) * 8] = rb[j];
+      lds_a[0][tid + 256 * j] = ra[j];
+      lds_b[0][tid + 256 * j] = rb[j];
     }
     __syncthreads();
     const int KT = K / TBK;
@@ -269,50 +289,40 @@ __global__ __launch_bounds__(256) void k_tile_bf16(KArgs a) {
       const int cur = kt & 1;
       const bool more = kt + 1 < KT;
       if (more) {
-        const int o = (kt + 1) * TBK / 8;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          ra[j] = va[j] ? ga[j][o] : zero;
-          rb[j] = gb[j][o];
+          ra[j] = va[j] ? *(const u32x4_t*)(ga[j] + (kt + 1) * TBK) : zero;
+          rb[j] = gb[j][(size_t)(kt + 1) * 2 * 64];
         }
       }
-      // two MFMA steps over BK = 64: lane reads 32 contiguous bytes per row
-      u32x4_t fa[4][2], fb[4][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16_t* pa = &lds_a[cur][(wm * 64 + i * 16 + c16) * TLD + 16 * q];
-        fa[i][0] = *(const u32x4_t*)pa;
-        fa[i][1] = *(const u32x4_t*)(pa + 8);
-      }
+      for (int s = 0; s < 2; ++s) {
+        u32x4_t fa[4], fb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int brow;
-        if (MODE == MODE_GATEUP)          // j 0,1: gate; j 2,3: up
-          brow = (j >> 1) * 64 + wn * 32 + (j & 1) * 16 + c16;
-        else
-          brow = wn * 64 + j * 16 + c16;
-        const bf16_t* pb = &lds_b[cur][brow * TLD + 16 * q];
-        fb[j][0] = *(const u32x4_t*)pb;
-        fb[j][1] = *(const u32x4_t*)(pb + 8);
-      }
+        for (int i = 0; i < 4; ++i) fa[i] = lds_a[cur][((wm * 4 + i) * 2 + s) * 64 + lane];
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+        for (int j = 0; j < 4; ++j) {
+          int cb;
+          if (MODE == MODE_GATEUP) cb = (j >> 1) * 4 + wn * 2 + (j & 1);
+          else cb = wn * 4 + j;
+          fb[j] = lds_b[cur][(cb * 2 + s) * 64 + lane];
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (i < nmb_valid)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(fa[i][s], fb[j][s], acc[i][j]);
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(fa[i], fb[j], acc[i][j]);
+      }
       if (more) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int c = tid + 256 * j;
-          *(u32x4_t*)&lds_a[cur ^ 1][(c >> 3) * TLD + (c & 7) * 8] = ra[j];
-          *(u32x4_t*)&lds_b[cur ^ 1][(c >> 3) * TLD + (c & 7) * 8] = rb[j];
+          lds_a[cur ^ 1][tid + 256 * j] = ra[j];
+          lds_b[cur ^ 1][tid + 256 * j] = rb[j];
         }
       }
       __syncthreads();
     }
-    // epilogue
+    const int c16 = lane & 15;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i >= nmb_valid) continue;
@@ -335,7 +345,8 @@ __global__ __launch_bounds__(256) void k_tile_bf16(KArgs a) {
 }
 
 // --------------------------------------------------------- fp32 recipe
-// Plain float32 FMA kernels: one thread per (row, output channel).
+// Plain float32 FMA kernels on natural output-major weights: one thread per
+// (row, output channel).
 template <int MODE>
 __global__ __launch_bounds__(256) void k_f32(KArgs a) {
   const int total_tiles = a.tile_count[0];
@@ -350,7 +361,9 @@ __global__ __launch_bounds__(256) void k_f32(KArgs a) {
     if (r >= td.z) continue;
     const int g = td.x, row = td.y + r;
     const bool sh = g == a.P;
-    const float* A = (const float*)(sh ? a.a_shared : a.a_routed) + (size_t)row * a.K;
+    const float* A;
+    if (sh) A = (const float*)a.a_shared + (size_t)row * a.K;
+    else A = (const float*)a.a_routed + (size_t)(a.a_rows ? a.a_rows[row] : row) * a.K;
     const float* W0 = (const float*)(sh ? a.w0_sh : a.w0_arr[g]) + (size_t)n * a.K;
     if (MODE == MODE_GATEUP) {
       const float* W1 = (const float*)(sh ? a.w1_sh : a.w1_arr[g]) + (size_t)n * a.K;
@@ -370,24 +383,39 @@ __global__ __launch_bounds__(256) void k_f32(KArgs a) {
   }
 }
 
-// -------------------------------------------------------------- driver
-size_t ffn_scratch_bytes(int H, int I, int P, int T, int cap, int has_shared,
-                         int act, int wdt) {
-  const size_t hrows = (size_t)cap + (has_shared ? T : 0);
-  size_t hb = act == MOE_F32 ? 4 : (wdt == MOE_FP8_E4M3 ? 1 : 2);
-  size_t b = moe_align256(hrows * I * hb);
-  if (wdt == MOE_FP8_E4M3) b += moe_align256(hrows * (I / 128) * sizeof(float));
-  // tiles: at most one per group plus one per 16 rows
-  const size_t max_tiles = (size_t)P + 1 + (hrows + 15) / 16 + 1;
-  b += moe_align256(max_tiles * sizeof(int4));
-  b += 256;
-  return b;
+// ------------------------------------------------------- weight packing
+// Natural output-major bf16 [R][C] -> packed 16 x 32 operand blocks (see the
+// top of this file).  One thread per 16-byte output chunk.
+__global__ __launch_bounds__(256) void k_pack_bf16(const bf16_t* __restrict__ src,
+                                                   int R, int C,
+                                                   u32x4_t* __restrict__ dst) {
+  const size_t total = (size_t)R * C / 8;
+  const int CB = C / 32;
+  for (size_t gi = (size_t)blockIdx.x * 256 + threadIdx.x; gi < total;
+       gi += (size_t)gridDim.x * 256) {
+    const size_t blk = gi >> 6;
+    const int lane = (int)(gi & 63);
+    const size_t rb = blk / CB, cb = blk - rb * CB;
+    const size_t r = rb * 16 + (lane & 15), c = cb * 32 + (lane >> 4) * 8;
+    dst[gi] = *(const u32x4_t*)(src + r * C + c);
+  }
 }
 
+hipError_t launch_pack_bf16(const bf16_t* src, int R, int C, void* dst,
+                            hipStream_t s) {
+  const size_t total = (size_t)R * C / 8;
+  if (total == 0) return hipSuccess;
+  size_t grid = (total + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  k_pack_bf16<<<(unsigned)grid, 256, 0, s>>>(src, R, C, (u32x4_t*)dst);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- driver
 hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   const int G = f.P + (f.has_shared ? 1 : 0);
   if (G == 0) return hipSuccess;
-  // The expected rows per routed group decide the kernel: a few rows per
+  // The expected rows per routed group choose the kernel: a few rows per
   // expert (decode) stream the weights; hundreds (prefill) tile through LDS.
   const bool f32 = f.act == MOE_F32;
   int BM;
@@ -417,6 +445,7 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   a.K = f.H;
   a.N = f.I;
   a.a_routed = f.a_routed;
+  a.a_rows = f.a_rows;
   a.a_shared = f.a_shared;
   a.w0_arr = w->w_gate;
   a.w1_arr = w->w_up;
@@ -432,7 +461,7 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   } else if (stream) {
     a.nb_per_tile = a.N / 64;
     long items = max_tiles * a.nb_per_tile;
-    long grid = items < cu * 12 ? items : cu * 12;
+    long grid = items < cu * 16 ? items : cu * 16;
     k_stream_bf16<MODE_GATEUP, 2><<<(unsigned)grid, 256, 0, s>>>(a);
   } else {
     a.nb_per_tile = a.N / 64;
@@ -448,6 +477,7 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   a.K = f.I;
   a.N = f.H;
   a.a_routed = f.h;
+  a.a_rows = nullptr;
   a.a_shared = (const char*)f.h + (size_t)f.cap * f.I * hb;
   a.w0_arr = w->w_down;
   a.w1_arr = nullptr;
@@ -463,7 +493,7 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   } else if (stream) {
     a.nb_per_tile = a.N / 64;
     long items = max_tiles * a.nb_per_tile;
-    long grid = items < cu * 12 ? items : cu * 12;
+    long grid = items < cu * 16 ? items : cu * 16;
     k_stream_bf16<MODE_DOWN, 2><<<(unsigned)grid, 256, 0, s>>>(a);
   } else {
     a.nb_per_tile = a.N / 128;

@@ -110,6 +110,12 @@ class DeviceLayer:
                 out[key] = codes
                 out["s" + key[1]] = scales
                 del t
+            elif self.p.weight_dtype == L.MOE_BF16:
+                rows, cols = t.shape
+                packed = torch.empty_like(t)
+                L.moe_prepack_weights(t, rows, cols, L.MOE_BF16, packed)
+                out[key] = packed
+                del t
             else:
                 out[key] = t
         return out

@@ -86,10 +86,12 @@ typedef struct {
 
 /* Expert weights.  w_gate, w_up, w_down (and the scales) are DEVICE arrays of
  * P device pointers, one per physical expert (replicas may alias).  Each
- * matrix is stored output-major, i.e. as the transpose of the math matrix:
+ * matrix is the transpose of the math matrix, i.e. output-major:
  *   gate, up: [I][H]  (row n holds the H weights of output channel n)
  *   down:     [H][I]
- * Element type = weight_dtype.  FP8 weights come with float32 scales, one per
+ * F32 weights are in this natural row-major layout.  BF16 weights must be in
+ * the packed operand layout written by moe_prepack_weights (same bytes,
+ * reordered into 16 x 32 blocks).  Element type = weight_dtype.  FP8 weights come with float32 scales, one per
  * 128 x 128 block of the stored matrix: gate/up [I/128][H/128], down
  * [H/128][I/128]; scales are NULL otherwise.  The sh_* members are plain
  * device pointers for the shared expert (NULL when has_shared = 0). */
@@ -226,6 +228,21 @@ MOE_API moe_status moe_layer_forward_timed(const moe_problem* p,
                                    int32_t* expert_counts, void* workspace,
                                    size_t ws_bytes, void* stream,
                                    void* const* events);
+
+/* One-time weight preparation for the BF16 recipe (not on the layer's path):
+ * reorder a natural output-major matrix src [rows][cols] (cols = the
+ * reduction: H for gate/up, I for down) into the packed operand layout the
+ * expert kernels stream.  The matrix is cut into 16 x 32 blocks; block
+ * (r/16, c/32) is stored at block index (r/16) * (cols/32) + c/32, 1 KiB per
+ * block; inside a block, 16-byte lane L = r%16 + 16 * ((c%32) / 8) holds the
+ * 8 consecutive elements with c%8 = 0..7.  16 output channels over the whole
+ * reduction thus form one contiguous run, and each 1 KiB block is one
+ * wavefront's matrix-core operand.  dtype must be MOE_BF16; rows % 16 == 0,
+ * cols % 32 == 0; src and dst are distinct device buffers of rows*cols
+ * elements. */
+MOE_API moe_status moe_prepack_weights(const void* src, int32_t rows,
+                                       int32_t cols, int32_t dtype, void* dst,
+                                       void* stream);
 
 /* One-time weight preparation for the FP8 recipe (not on the layer's path):
  * quantise a float32 matrix [rows][cols] to E4M3 with one float32 scale per

@@ -153,3 +153,14 @@ def test_hottest_map_matches_oracle(counts, red):
 def test_hottest_map_rejects_bad_arguments():
     with pytest.raises(m.MoeError):
         m.moe_eplb_hottest_map([1, 2], 3)
+
+
+def test_prepack_checks_arguments():
+    assert m.moe_prepack_weights(256, 16, 30, L.MOE_BF16, 512, stream=0,
+                                 check=False) == L.MOE_ERR_INVALID_ARGUMENT
+    assert m.moe_prepack_weights(256, 16, 32, L.MOE_F32, 512, stream=0,
+                                 check=False) == L.MOE_ERR_UNSUPPORTED
+    assert m.moe_prepack_weights(256, 16, 32, L.MOE_BF16, 256, stream=0,
+                                 check=False) == L.MOE_ERR_INVALID_ARGUMENT
+    assert m.moe_prepack_weights(None, 0, 32, L.MOE_BF16, None, stream=0,
+                                 check=False) == L.MOE_OK
