@@ -96,9 +96,11 @@ moe_status launch_ffn_common(const moe_problem* p, const void* x_perm,
                              const moe_weights* w, float* y_perm,
                              float* y_shared, const FfnScratch& fs,
                              hipStream_t s, hipEvent_t* events = nullptr,
-                             const int32_t* a_rows = nullptr) {
+                             const int32_t* a_rows = nullptr,
+                             bool tiles_ready = false) {
   FfnArgs a{};
   a.a_rows = a_rows;
+  a.tiles_ready = tiles_ready;
   a.H = p->H;
   a.I = p->I;
   a.P = p->num_physical;
@@ -146,7 +148,8 @@ moe_status dispatch_impl(const moe_problem* p, const void* x,
                          int32_t* row_token, float* row_weight,
                          int32_t* pair_row, const DispatchScratch& d,
                          hipStream_t s, hipEvent_t ev_index = nullptr,
-                         bool materialize = true) {
+                         bool materialize = true,
+                         const SmallExtras* extras = nullptr) {
   DispatchArgs a{};
   a.T = p->T;
   a.k = p->k;
@@ -165,7 +168,15 @@ moe_status dispatch_impl(const moe_problem* p, const void* x,
   a.row_token = row_token;
   a.row_weight = row_weight;
   a.pair_row = pair_row;
-  hipError_t e = launch_dispatch_index(a, s);
+  hipError_t e;
+  if (dispatch_small_ok(p->T, p->E, p->num_local, p->num_physical)) {
+    SmallExtras x{};
+    x.E = p->E;
+    if (extras) x = *extras;
+    e = launch_dispatch_small(a, x, s);
+  } else {
+    e = launch_dispatch_index(a, s);
+  }
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (ev_index) hipEventRecord(ev_index, s);
   const int cap = (int)cap_rows(p);
@@ -408,15 +419,28 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
   LayerScratch L = carve_layer(c, p);
   if (ev) hipEventRecord(ev[0], s);
   int32_t* counts = expert_counts ? expert_counts : L.counts;
-  if (launch_fill_i32(counts, 0, (size_t)p->E, s) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_route_topk(logits, bias, p->T, p->E, p->k, L.ids, L.tw, counts,
-                        s) != hipSuccess)
+  // Small batches: the single-workgroup dispatch also counts the experts
+  // and writes the FFN tile list, so neither needs a launch of its own.
+  const bool small = dispatch_small_ok(p->T, p->E, p->num_local, p->num_physical);
+  SmallExtras extras{};
+  extras.E = p->E;
+  if (small) {
+    extras.counts = counts;
+    extras.tiles = L.f.tiles;
+    extras.tile_count = L.f.tile_count;
+    extras.BM = ffn_tile_rows(p->act_dtype, rows_hint(p));
+    extras.has_shared = p->has_shared;
+  } else if (launch_fill_i32(counts, 0, (size_t)p->E, s) != hipSuccess) {
+    return MOE_ERR_HIP;
+  }
+  if (launch_route_topk(logits, bias, p->T, p->E, p->k, L.ids, L.tw,
+                        small ? nullptr : counts, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (ev) hipEventRecord(ev[1], s);
   st = dispatch_impl(p, x, L.ids, L.tw, l2p, replica_count, L.x_perm,
                      L.x_perm_scales, L.offsets, L.row_token, L.row_weight,
                      L.pair_row, L.d, s, ev ? ev[2] : nullptr,
-                     /*materialize=*/false);
+                     /*materialize=*/false, small ? &extras : nullptr);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[3], s);
   // The expert kernels read each routed row straight from the token rows
@@ -428,7 +452,7 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
                          p->has_shared ? xs : nullptr,
                          p->has_shared && fp8 ? L.d.xs : nullptr, w, L.y_perm,
                          L.y_shared, L.f, s, ev ? ev + 4 : nullptr,
-                         L.row_token);
+                         L.row_token, /*tiles_ready=*/small);
   if (st != MOE_OK) return st;
   st = hip_status(launch_combine(L.y_perm, L.pair_row, L.tw,
                                  p->has_shared ? L.y_shared : nullptr, p->T,

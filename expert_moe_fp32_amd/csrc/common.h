@@ -95,6 +95,19 @@ struct DispatchArgs {
 int dispatch_blocks(int T);
 hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s);
 
+// single-workgroup variant for small batches; optionally also writes the
+// expert counts over all E and the expert FFN's tile list
+struct SmallExtras {
+  int E;
+  int32_t* counts;        // [E] or null
+  int4* tiles;            // or null
+  int32_t* tile_count;
+  int BM, has_shared;
+};
+bool dispatch_small_ok(int T, int E, int L, int P);
+hipError_t launch_dispatch_small(const DispatchArgs& a, const SmallExtras& x,
+                                 hipStream_t s);
+
 // x_perm[r] = x[row_token[r]] for r < offsets[P]; row_bytes % 16 == 0
 hipError_t launch_gather_rows(const void* x, size_t row_bytes,
                               const int32_t* row_token,
@@ -142,11 +155,12 @@ struct FfnArgs {
   int4* tiles;                        // tile list scratch
   int32_t* tile_count;                // [2] scratch
   int max_tiles;
+  bool tiles_ready;                   // tile list already written
   hipEvent_t* events;                 // optional: after tiles, gate/up, down
 };
-size_t ffn_scratch_bytes(int H, int I, int P, int T, int cap, int has_shared,
-                         int act, int wdt);
 hipError_t launch_ffn(FfnArgs& a, hipStream_t s);
+// rows per tile the FFN uses for this recipe and expected group size
+int ffn_tile_rows(int act, int rows_hint);
 
 // natural output-major bf16 [R][C] -> packed 16x32 operand blocks
 hipError_t launch_pack_bf16(const bf16_t* src, int R, int C, void* dst,

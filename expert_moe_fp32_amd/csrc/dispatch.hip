@@ -163,6 +163,143 @@ __global__ __launch_bounds__(256) void k_permute(
   }
 }
 
+// ----------------------------------------- single-workgroup small batch
+// For T <= 1024 one workgroup (one thread per token) does everything the
+// three kernels above do, plus the expert counts over all E and, when asked,
+// the expert FFN's tile list: fewer dependent launches on the decode path.
+// Same positions as the multi-block path: the pair's rank inside its
+// 64-token wavefront comes from a ballot, earlier wavefronts from LDS.
+static constexpr int kSmallT = 1024, kSmallL = 256;
+
+bool dispatch_small_ok(int T, int E, int L, int P) {
+  return T <= kSmallT && L <= kSmallL && E <= MOE_EMAX && P <= MOE_LMAX;
+}
+
+__global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
+                                                         SmallExtras x) {
+  __shared__ int32_t cnt[MOE_EMAX];
+  __shared__ int32_t pc[MOE_LMAX + 1];
+  __shared__ int32_t tb[MOE_LMAX + 2];
+  __shared__ int32_t wpre[16 * kSmallL];
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+  const int T = a.T, k = a.k, L = a.num_local, P = a.P;
+  for (int i = t; i < x.E; i += 1024) cnt[i] = 0;
+  for (int i = t; i <= P; i += 1024) pc[i] = 0;
+  __syncthreads();
+  int le[MOE_KMAX], rank[MOE_KMAX];
+  bool any_local = false;
+#pragma unroll
+  for (int j = 0; j < MOE_KMAX; ++j) {
+    le[j] = -1;
+    rank[j] = 0;
+    if (j < k && t < T) {
+      const int gid = a.ids[(size_t)t * k + j];
+      atomicAdd(&cnt[gid], 1);
+      const int e = gid - a.expert_begin;
+      if (e >= 0 && e < L) {
+        le[j] = e;
+        any_local = true;
+      }
+    }
+  }
+  const bool wave_has = __ballot(any_local) != 0ull;
+  const uint64_t lt = lanemask_lt();
+  for (int e = 0; e < L; ++e) {
+    int c = 0;
+    if (wave_has) {
+      bool has = false;
+#pragma unroll
+      for (int j = 0; j < MOE_KMAX; ++j) has |= le[j] == e;
+      const uint64_t m = __ballot(has);
+      c = __popcll(m);
+      const int below = __popcll(m & lt);
+#pragma unroll
+      for (int j = 0; j < MOE_KMAX; ++j)
+        if (le[j] == e) rank[j] = below;
+    }
+    if (lane == 0) wpre[wv * kSmallL + e] = c;
+  }
+  __syncthreads();
+  if (x.counts)
+    for (int i = t; i < x.E; i += 1024) x.counts[i] = cnt[i];
+  if (t < L) {
+    const int e = t;
+    int run = 0;                           // exclusive prefix over wavefronts
+    for (int v = 0; v < 16; ++v) {
+      const int c = wpre[v * kSmallL + e];
+      wpre[v * kSmallL + e] = run;
+      run += c;
+    }
+    const int R = a.rep ? min(max(a.rep[e], 1), a.max_rep) : 1;
+    for (int r = 0; r < R; ++r) {
+      const int p = a.l2p ? a.l2p[e * a.max_rep + r] : e;
+      if (p >= 0 && p < P) pc[p] = run > r ? (run - r + R - 1) / R : 0;
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int p = 0; p < P; ++p) {
+      const int c = pc[p];
+      pc[p] = run;
+      a.offsets[p] = run;
+      run += c;
+    }
+    pc[P] = run;
+    a.offsets[P] = run;
+    if (x.tiles) {                         // tile list of the expert FFN
+      const int G = P + (x.has_shared ? 1 : 0);
+      int nt = 0;
+      for (int g = 0; g < G; ++g) {
+        tb[g] = nt;
+        const int rows = g < P ? pc[g + 1] - pc[g] : T;
+        nt += (rows + x.BM - 1) / x.BM;
+      }
+      tb[G] = nt;
+      x.tile_count[0] = nt;
+    }
+  }
+  __syncthreads();
+  if (x.tiles) {
+    const int G = P + (x.has_shared ? 1 : 0);
+    for (int g = t; g < G; g += 1024) {
+      const int start = g < P ? pc[g] : 0;
+      const int rows = g < P ? pc[g + 1] - start : T;
+      int i = tb[g];
+      for (int r = 0; r < rows; r += x.BM, ++i)
+        x.tiles[i] = make_int4(g, start + r, min(x.BM, rows - r), 0);
+    }
+  }
+  if (t >= T) return;
+#pragma unroll
+  for (int j = 0; j < MOE_KMAX; ++j) {
+    if (j >= k) break;
+    const size_t o = (size_t)t * k + j;
+    const int e = le[j];
+    if (e < 0) {
+      a.pair_row[o] = -1;
+      continue;
+    }
+    const int n = wpre[wv * kSmallL + e] + rank[j];
+    const int R = a.rep ? min(max(a.rep[e], 1), a.max_rep) : 1;
+    const int p = a.l2p ? a.l2p[e * a.max_rep + (n % R)] : e;
+    if (p < 0 || p >= P) {
+      a.pair_row[o] = -1;
+      continue;
+    }
+    const int row = pc[p] + n / R;
+    a.pair_row[o] = row;
+    a.row_token[row] = t;
+    a.row_weight[row] = a.w[o];
+  }
+}
+
+hipError_t launch_dispatch_small(const DispatchArgs& a, const SmallExtras& x,
+                                 hipStream_t s) {
+  k_dispatch_small<<<1, 1024, 0, s>>>(a, x);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s) {
   const int nblk = dispatch_blocks(a.T);
   const size_t lds = sizeof(int32_t) * 4 * a.num_local;

@@ -412,24 +412,22 @@ hipError_t launch_pack_bf16(const bf16_t* src, int R, int C, void* dst,
 }
 
 // -------------------------------------------------------------- driver
+int ffn_tile_rows(int act, int rows_hint) {
+  if (act == MOE_F32) return TBM;
+  return rows_hint <= 32 ? 32 : TBM;
+}
+
 hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   const int G = f.P + (f.has_shared ? 1 : 0);
   if (G == 0) return hipSuccess;
   // The expected rows per routed group choose the kernel: a few rows per
   // expert (decode) stream the weights; hundreds (prefill) tile through LDS.
   const bool f32 = f.act == MOE_F32;
-  int BM;
-  bool stream = false;
-  if (f32) {
-    BM = TBM;
-  } else if (f.rows_hint <= 32) {
-    BM = 32;
-    stream = true;
-  } else {
-    BM = TBM;
-  }
-  k_build_tiles<<<1, 1024, 0, s>>>(f.offsets, f.P, f.has_shared, f.T, BM,
-                                   f.tiles, f.tile_count);
+  const int BM = ffn_tile_rows(f.act, f.rows_hint);
+  const bool stream = !f32 && BM == 32;
+  if (!f.tiles_ready)
+    k_build_tiles<<<1, 1024, 0, s>>>(f.offsets, f.P, f.has_shared, f.T, BM,
+                                     f.tiles, f.tile_count);
   if (f.events) hipEventRecord(f.events[0], s);
   // bound on the tile count for the grid size
   const long hrows = (long)f.cap + (f.has_shared ? f.T : 0);
