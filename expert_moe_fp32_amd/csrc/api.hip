@@ -59,6 +59,7 @@ DispatchScratch carve_dispatch(Carver& c, const moe_problem* p) {
 struct FfnScratch {
   void* h;
   float* h_scales;
+  float* h32;
   int4* tiles;
   int32_t* tile_count;
   int max_tiles;
@@ -71,8 +72,10 @@ FfnScratch carve_ffn(Carver& c, const moe_problem* p) {
   const size_t hb = p->act_dtype == MOE_F32 ? 4
                     : (p->weight_dtype == MOE_FP8_E4M3 ? 1 : 2);
   f.h = c.take<char>(hrows * p->I * hb);
-  if (p->weight_dtype == MOE_FP8_E4M3)
+  if (p->weight_dtype == MOE_FP8_E4M3) {
     f.h_scales = c.take<float>(hrows * (p->I / 128));
+    f.h32 = c.take<float>(hrows * p->I);
+  }
   f.max_tiles = (int)(p->num_physical + 1 + (hrows + 15) / 16 + 1);
   f.tiles = c.take<int4>((size_t)f.max_tiles);
   f.tile_count = c.take<int32_t>(4);
@@ -81,7 +84,7 @@ FfnScratch carve_ffn(Carver& c, const moe_problem* p) {
 
 // recipes whose expert kernels exist
 bool ffn_built(const moe_problem* p) {
-  return p->weight_dtype != MOE_FP8_E4M3;
+  return p != nullptr;
 }
 
 int rows_hint(const moe_problem* p) {
@@ -118,6 +121,7 @@ moe_status launch_ffn_common(const moe_problem* p, const void* x_perm,
   a.w = w;
   a.h = fs.h;
   a.h_scales = fs.h_scales;
+  a.h32 = fs.h32;
   a.y_routed = y_perm;
   a.y_shared = y_shared;
   a.tiles = fs.tiles;
@@ -428,7 +432,7 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
     extras.counts = counts;
     extras.tiles = L.f.tiles;
     extras.tile_count = L.f.tile_count;
-    extras.BM = ffn_tile_rows(p->act_dtype, rows_hint(p));
+    extras.BM = ffn_tile_rows(p->act_dtype, p->weight_dtype, rows_hint(p));
     extras.has_shared = p->has_shared;
   } else if (launch_fill_i32(counts, 0, (size_t)p->E, s) != hipSuccess) {
     return MOE_ERR_HIP;
@@ -491,10 +495,13 @@ moe_status moe_layer_forward_timed(const moe_problem* p, const float* logits,
 moe_status moe_prepack_weights(const void* src, int32_t rows, int32_t cols,
                                int32_t dtype, void* dst, void* stream) {
   if (rows < 0 || cols < 0) return MOE_ERR_INVALID_ARGUMENT;
-  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (rows % 16 || cols % 32) return MOE_ERR_INVALID_ARGUMENT;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  const int cblk = dtype == MOE_BF16 ? 32 : 128;
+  if (rows % 16 || cols % cblk) return MOE_ERR_INVALID_ARGUMENT;
   if (rows == 0 || cols == 0) return MOE_OK;
   if (!src || !dst || src == dst) return MOE_ERR_INVALID_ARGUMENT;
+  if (dtype == MOE_FP8_E4M3)
+    return hip_status(launch_pack_fp8((const uint8_t*)src, rows, cols, dst, S(stream)));
   return hip_status(launch_pack_bf16((const bf16_t*)src, rows, cols, dst, S(stream)));
 }
 

@@ -150,6 +150,7 @@ struct FfnArgs {
   const moe_weights* w;               // host copy of the struct
   void* h;                            // [cap + T][I] intermediate
   float* h_scales;                    // fp8: [cap + T][I/128]
+  float* h32;                         // fp8: float32 h before quantisation
   float* y_routed;                    // [cap][H]
   float* y_shared;                    // [T][H]
   int4* tiles;                        // tile list scratch
@@ -159,11 +160,18 @@ struct FfnArgs {
   hipEvent_t* events;                 // optional: after tiles, gate/up, down
 };
 hipError_t launch_ffn(FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_fp8(FfnArgs& a, hipStream_t s);
 // rows per tile the FFN uses for this recipe and expected group size
-int ffn_tile_rows(int act, int rows_hint);
+int ffn_tile_rows(int act, int wdt, int rows_hint);
+hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
+                              int T, int BM, int4* tiles, int32_t* count,
+                              hipStream_t s);
 
-// natural output-major bf16 [R][C] -> packed 16x32 operand blocks
+// natural output-major [R][C] -> packed operand blocks (bf16: 16x32 blocks;
+// fp8: 16x128 blocks)
 hipError_t launch_pack_bf16(const bf16_t* src, int R, int C, void* dst,
                             hipStream_t s);
+hipError_t launch_pack_fp8(const uint8_t* src, int R, int C, void* dst,
+                           hipStream_t s);
 
 }  // namespace moe

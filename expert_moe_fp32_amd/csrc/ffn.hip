@@ -412,18 +412,26 @@ hipError_t launch_pack_bf16(const bf16_t* src, int R, int C, void* dst,
 }
 
 // -------------------------------------------------------------- driver
-int ffn_tile_rows(int act, int rows_hint) {
-  if (act == MOE_F32) return TBM;
+int ffn_tile_rows(int act, int wdt, int rows_hint) {
+  if (act == MOE_F32 || wdt == MOE_FP8_E4M3) return TBM;
   return rows_hint <= 32 ? 32 : TBM;
 }
 
+hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
+                              int T, int BM, int4* tiles, int32_t* count,
+                              hipStream_t s) {
+  k_build_tiles<<<1, 1024, 0, s>>>(offsets, P, has_shared, T, BM, tiles, count);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
+  if (f.wdt == MOE_FP8_E4M3) return launch_ffn_fp8(f, s);
   const int G = f.P + (f.has_shared ? 1 : 0);
   if (G == 0) return hipSuccess;
   // The expected rows per routed group choose the kernel: a few rows per
   // expert (decode) stream the weights; hundreds (prefill) tile through LDS.
   const bool f32 = f.act == MOE_F32;
-  const int BM = ffn_tile_rows(f.act, f.rows_hint);
+  const int BM = ffn_tile_rows(f.act, f.wdt, f.rows_hint);
   const bool stream = !f32 && BM == 32;
   if (!f.tiles_ready)
     k_build_tiles<<<1, 1024, 0, s>>>(f.offsets, f.P, f.has_shared, f.T, BM,

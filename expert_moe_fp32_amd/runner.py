@@ -65,9 +65,10 @@ class DeviceLayer:
                  shared: Optional[dict] = None,
                  phys_to_logical: Optional[Sequence[int]] = None,
                  l2p=None, replica_count=None, copy_replicas=True,
-                 device="cuda"):
+                 device="cuda", keep_codes=False):
         self.p = problem
         self.device = device
+        self.keep_codes = keep_codes   # fp8: also keep unpacked codes
         P = problem.num_physical
         if phys_to_logical is None:
             phys_to_logical = list(range(P))
@@ -107,7 +108,11 @@ class DeviceLayer:
                 scales = torch.empty((rows // 128, cols // 128),
                                      dtype=torch.float32, device=self.device)
                 L.moe_quantize_fp8_blocks(t, rows, cols, 128, codes, scales)
-                out[key] = codes
+                packed = torch.empty_like(codes)
+                L.moe_prepack_weights(codes, rows, cols, L.MOE_FP8_E4M3, packed)
+                if self.keep_codes:
+                    out["codes_" + key] = codes
+                out[key] = packed
                 out["s" + key[1]] = scales
                 del t
             elif self.p.weight_dtype == L.MOE_BF16:

@@ -164,3 +164,10 @@ def test_prepack_checks_arguments():
                                  check=False) == L.MOE_ERR_INVALID_ARGUMENT
     assert m.moe_prepack_weights(None, 0, 32, L.MOE_BF16, None, stream=0,
                                  check=False) == L.MOE_OK
+
+
+def test_prepack_fp8_checks_arguments():
+    assert m.moe_prepack_weights(256, 16, 64, L.MOE_FP8_E4M3, 512, stream=0,
+                                 check=False) == L.MOE_ERR_INVALID_ARGUMENT
+    assert m.moe_prepack_weights(256, 8, 128, L.MOE_FP8_E4M3, 512, stream=0,
+                                 check=False) == L.MOE_ERR_INVALID_ARGUMENT

@@ -1,0 +1,96 @@
+"""FP8 recipe on the GPU against the oracle: block-quantised weight codes and
+scales bit-exact, packed layout as documented, layer outputs within
+4e-2 x RMS (after the bf16 output rounding)."""
+import numpy as np
+import pytest
+
+from oracle import fp8 as ofp8, moe as omoe
+from synth import make_workload
+
+from .helpers import BARS, check_output, device_layer, out_to_f64
+from .test_gpu_layer import oracle_out, sample_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def test_weight_quantiser_bit_exact():
+    import torch
+    import expert_moe_fp32_amd as m
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((384, 256)) * 0.02).astype(np.float32)
+    w[:128, 128:] = 0.0                       # an all-zero block
+    w[200, 7] = 3.0                           # a block with one outlier
+    dw = torch.from_numpy(w).cuda()
+    codes = torch.empty((384, 256), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((3, 2), dtype=torch.float32, device="cuda")
+    m.moe_quantize_fp8_blocks(dw, 384, 256, 128, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = ofp8.quantize_blocks_2d(w, 128)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
+def packed_fp8_reference(c: np.ndarray) -> np.ndarray:
+    """Block (r/16, c/128) of 2 KiB at (r/16)*(C/128) + c/128; lane
+    L = r%16 + 16*((c%128)//32); byte (c%32) of its slot at
+    (c%32 >= 16)*1024 + L*16 + c%16."""
+    R, C = c.shape
+    out = np.empty(R * C, dtype=np.uint8)
+    for r in range(R):
+        for k in range(C):
+            blk = (r // 16) * (C // 128) + k // 128
+            L = r % 16 + 16 * ((k % 128) // 32)
+            off = ((k % 32) // 16) * 1024 + L * 16 + k % 16
+            out[blk * 2048 + off] = c[r, k]
+    return out
+
+
+def test_prepack_fp8_layout():
+    import torch
+    import expert_moe_fp32_amd as m
+    from expert_moe_fp32_amd import _lib as L
+    rng = np.random.default_rng(3)
+    c = rng.integers(0, 256, size=(32, 256), dtype=np.uint8)
+    src = torch.from_numpy(c).cuda()
+    dst = torch.zeros_like(src)
+    m.moe_prepack_weights(src, 32, 256, L.MOE_FP8_E4M3, dst)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy().ravel(), packed_fp8_reference(c))
+
+
+def run_fp8_layer(wl):
+    import torch
+    from expert_moe_fp32_amd.runner import to_dev
+    dl = device_layer(wl)
+    b = dl.buffers()
+    dl.forward(b, to_dev(wl.logits), None if wl.bias is None else to_dev(wl.bias),
+               to_dev(wl.x))
+    torch.cuda.synchronize()
+    out = out_to_f64(b, wl)
+    del dl, b
+    torch.cuda.empty_cache()
+    return out
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=200, H=256, I=256, E=16, num_local=8, k=4),            # ragged tiles
+    dict(T=40, H=384, I=128, E=64, num_local=16, k=4),            # few rows
+    dict(T=300, H=256, I=128, E=8, num_local=8, k=2, shared=True),  # shared
+])
+def test_fp8_layer_reduced(kw):
+    wl = make_workload("fp8", seed=31, **kw)
+    print(f"layer {wl.describe()}", flush=True)
+    out = run_fp8_layer(wl)
+    ref = oracle_out(wl)
+    r = check_output(out, ref.out, wl.out, BARS["fp8"], wl.describe())
+    print(f"  max|err|/RMS = {r:.3e}")
+
+
+def test_fp8_full_sampled():
+    wl = make_workload("fp8", seed=0)
+    print(f"layer {wl.describe()}", flush=True)
+    out = run_fp8_layer(wl)
+    tok = sample_tokens(wl.T, 12, seed=2)
+    ref = oracle_out(wl, tokens=tok)
+    r = check_output(out[tok], ref.out[tok], wl.out, BARS["fp8"], "fp8")
+    print(f"  max|err|/RMS = {r:.3e}")
