@@ -61,6 +61,7 @@ struct FfnScratch {
   float* h_scales;
   float* h32;
   int4* tiles;
+  int4* tiles_down;
   int32_t* tile_count;
   int max_tiles;
 };
@@ -78,6 +79,8 @@ FfnScratch carve_ffn(Carver& c, const moe_problem* p) {
   }
   f.max_tiles = (int)(p->num_physical + 1 + (hrows + 15) / 16 + 1);
   f.tiles = c.take<int4>((size_t)f.max_tiles);
+  // 128-row tiles: at most one partial tile per group
+  f.tiles_down = c.take<int4>((size_t)p->num_physical + 2 + hrows / 128);
   f.tile_count = c.take<int32_t>(4);
   return f;
 }
@@ -125,6 +128,7 @@ moe_status launch_ffn_common(const moe_problem* p, const void* x_perm,
   a.y_routed = y_perm;
   a.y_shared = y_shared;
   a.tiles = fs.tiles;
+  a.tiles_down = fs.tiles_down;
   a.tile_count = fs.tile_count;
   a.max_tiles = fs.max_tiles;
   a.events = events;
@@ -432,7 +436,8 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
     extras.counts = counts;
     extras.tiles = L.f.tiles;
     extras.tile_count = L.f.tile_count;
-    extras.BM = ffn_tile_rows(p->act_dtype, p->weight_dtype, rows_hint(p));
+    extras.BM = ffn_tile_rows(p->act_dtype, p->weight_dtype, rows_hint(p),
+                              p->H, &extras.balanced);
     extras.has_shared = p->has_shared;
   } else if (launch_fill_i32(counts, 0, (size_t)p->E, s) != hipSuccess) {
     return MOE_ERR_HIP;

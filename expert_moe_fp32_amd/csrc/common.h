@@ -68,6 +68,19 @@ __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
   return __uint_as_float(__float_as_uint(v) | s);
 }
 
+// Rows per tile and tile count for a group of `rows` rows: tiles of BM rows,
+// or (balanced) ceil(rows / BM) near-equal tiles rounded up to 16 rows.
+__device__ __forceinline__ int tile_split(int rows, int BM, int balanced,
+                                          int* per) {
+  int p = BM;
+  if (balanced && rows > 0) {
+    const int nt = (rows + BM - 1) / BM;
+    p = (((rows + nt - 1) / nt) + 15) & ~15;
+  }
+  *per = p;
+  return (rows + p - 1) / p;
+}
+
 static inline size_t moe_align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 static inline int moe_ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
@@ -103,6 +116,7 @@ struct SmallExtras {
   int4* tiles;            // or null
   int32_t* tile_count;
   int BM, has_shared;
+  int balanced;           // near-equal tiles (multiples of 16 rows)
 };
 bool dispatch_small_ok(int T, int E, int L, int P);
 hipError_t launch_dispatch_small(const DispatchArgs& a, const SmallExtras& x,
@@ -154,15 +168,20 @@ struct FfnArgs {
   float* y_routed;                    // [cap][H]
   float* y_shared;                    // [T][H]
   int4* tiles;                        // tile list scratch
-  int32_t* tile_count;                // [2] scratch
+  int4* tiles_down;                   // second list (128-row tiles for down)
+  int32_t* tile_count;                // [2] scratch: counts of the lists
   int max_tiles;
   bool tiles_ready;                   // tile list already written
   hipEvent_t* events;                 // optional: after tiles, gate/up, down
 };
 hipError_t launch_ffn(FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_fp8(FfnArgs& a, hipStream_t s);
-// rows per tile the FFN uses for this recipe and expected group size
-int ffn_tile_rows(int act, int wdt, int rows_hint);
+// rows per tile the FFN uses for this recipe and expected group size; sets
+// *balanced when a group's tiles are near-equal multiples of 16 rows
+int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int* balanced);
+// gate/up LDS-ring GEMM over a list of tiles of up to gemm_tile_rows() rows
+hipError_t launch_gemm_bf16_gateup(const FfnArgs& f, hipStream_t s);
+int gemm_tile_rows();
 hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
                               int T, int BM, int4* tiles, int32_t* count,
                               hipStream_t s);

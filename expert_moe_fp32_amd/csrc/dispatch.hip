@@ -253,7 +253,8 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
       for (int g = 0; g < G; ++g) {
         tb[g] = nt;
         const int rows = g < P ? pc[g + 1] - pc[g] : T;
-        nt += (rows + x.BM - 1) / x.BM;
+        int per;
+        nt += tile_split(rows, x.BM, x.balanced, &per);
       }
       tb[G] = nt;
       x.tile_count[0] = nt;
@@ -265,9 +266,12 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
     for (int g = t; g < G; g += 1024) {
       const int start = g < P ? pc[g] : 0;
       const int rows = g < P ? pc[g + 1] - start : T;
+      if (rows == 0) continue;
+      int per;
+      tile_split(rows, x.BM, x.balanced, &per);
       int i = tb[g];
-      for (int r = 0; r < rows; r += x.BM, ++i)
-        x.tiles[i] = make_int4(g, start + r, min(x.BM, rows - r), 0);
+      for (int r = 0; r < rows; r += per, ++i)
+        x.tiles[i] = make_int4(g, start + r, min(per, rows - r), 0);
     }
   }
   if (t >= T) return;

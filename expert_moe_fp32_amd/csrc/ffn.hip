@@ -61,28 +61,43 @@ struct KArgs {
 // One workgroup.  Group g < P has offsets[g+1]-offsets[g] rows starting at
 // row offsets[g]; group P (shared) has T rows starting at 0.  Output:
 // tiles[i] = {group, first row, rows, 0}, count[0] = number of tiles.
+// Writes the tile list for tiles of BM rows (balanced: tile_split's
+// near-equal tiles) and, when tiles2 is non-null, a second plain list for
+// tiles of BM2 rows, each with its count.
 __global__ __launch_bounds__(1024) void k_build_tiles(
     const int32_t* __restrict__ offsets, int P, int has_shared, int T, int BM,
-    int4* __restrict__ tiles, int32_t* __restrict__ count) {
-  __shared__ int32_t base[MOE_LMAX + 2];
+    int balanced, int4* __restrict__ tiles, int32_t* __restrict__ count,
+    int BM2, int4* __restrict__ tiles2, int32_t* __restrict__ count2) {
+  __shared__ int32_t base[2][MOE_LMAX + 2];
   const int G = P + (has_shared ? 1 : 0);
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
     const int rows = g < P ? offsets[g + 1] - offsets[g] : T;
-    base[g + 1] = (rows + BM - 1) / BM;
+    int per;
+    base[0][g + 1] = tile_split(rows, BM, balanced, &per);
+    base[1][g + 1] = (rows + BM2 - 1) / BM2;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    base[0] = 0;
-    for (int g = 0; g < G; ++g) base[g + 1] += base[g];
-    count[0] = base[G];
+  if (threadIdx.x < 2) {
+    int32_t* b = base[threadIdx.x];
+    b[0] = 0;
+    for (int g = 0; g < G; ++g) b[g + 1] += b[g];
+    if (threadIdx.x == 0) count[0] = b[G];
+    else if (tiles2) count2[0] = b[G];
   }
   __syncthreads();
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
     const int start = g < P ? offsets[g] : 0;
     const int rows = g < P ? offsets[g + 1] - start : T;
-    int i = base[g];
-    for (int r = 0; r < rows; r += BM, ++i)
-      tiles[i] = make_int4(g, start + r, min(BM, rows - r), 0);
+    int per;
+    tile_split(rows, BM, balanced, &per);
+    int i = base[0][g];
+    for (int r = 0; r < rows; r += per, ++i)
+      tiles[i] = make_int4(g, start + r, min(per, rows - r), 0);
+    if (tiles2) {
+      i = base[1][g];
+      for (int r = 0; r < rows; r += BM2, ++i)
+        tiles2[i] = make_int4(g, start + r, min(BM2, rows - r), 0);
+    }
   }
 }
 
@@ -412,15 +427,26 @@ hipError_t launch_pack_bf16(const bf16_t* src, int R, int C, void* dst,
 }
 
 // -------------------------------------------------------------- driver
-int ffn_tile_rows(int act, int wdt, int rows_hint) {
+// Kernel choice for the bf16 recipe: the weight-streaming kernel for a few
+// rows per group; for hundreds (prefill) the 256 x 256 LDS-ring GEMM for
+// gate/up (balanced tiles of up to 256 rows) and the 128 x 128 tiled kernel
+// for down (its own list of 128-row tiles).
+static bool bf16_streaming(int rows_hint) { return rows_hint <= 32; }
+
+int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int* balanced) {
+  (void)H;
+  *balanced = 0;
   if (act == MOE_F32 || wdt == MOE_FP8_E4M3) return TBM;
-  return rows_hint <= 32 ? 32 : TBM;
+  if (bf16_streaming(rows_hint)) return 32;
+  *balanced = 1;
+  return gemm_tile_rows();
 }
 
 hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
                               int T, int BM, int4* tiles, int32_t* count,
                               hipStream_t s) {
-  k_build_tiles<<<1, 1024, 0, s>>>(offsets, P, has_shared, T, BM, tiles, count);
+  k_build_tiles<<<1, 1024, 0, s>>>(offsets, P, has_shared, T, BM, 0, tiles,
+                                   count, BM, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -431,11 +457,21 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   // The expected rows per routed group choose the kernel: a few rows per
   // expert (decode) stream the weights; hundreds (prefill) tile through LDS.
   const bool f32 = f.act == MOE_F32;
-  const int BM = ffn_tile_rows(f.act, f.wdt, f.rows_hint);
+  int balanced;
+  const int BM = ffn_tile_rows(f.act, f.wdt, f.rows_hint, f.H, &balanced);
   const bool stream = !f32 && BM == 32;
+  const bool ring = !f32 && balanced;     // tiles of up to 256 rows
+  // the ring GEMM's list (or the only list), plus down's 128-row list; a
+  // list already written by the dispatch is the first one
   if (!f.tiles_ready)
     k_build_tiles<<<1, 1024, 0, s>>>(f.offsets, f.P, f.has_shared, f.T, BM,
-                                     f.tiles, f.tile_count);
+                                     balanced, f.tiles, f.tile_count, TBM,
+                                     ring ? f.tiles_down : nullptr,
+                                     f.tile_count + 1);
+  else if (ring)
+    k_build_tiles<<<1, 1024, 0, s>>>(f.offsets, f.P, f.has_shared, f.T, TBM, 0,
+                                     f.tiles_down, f.tile_count + 1, TBM,
+                                     nullptr, nullptr);
   if (f.events) hipEventRecord(f.events[0], s);
   // bound on the tile count for the grid size
   const long hrows = (long)f.cap + (f.has_shared ? f.T : 0);
@@ -469,6 +505,9 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
     long items = max_tiles * a.nb_per_tile;
     long grid = items < cu * 16 ? items : cu * 16;
     k_stream_bf16<MODE_GATEUP, 2><<<(unsigned)grid, 256, 0, s>>>(a);
+  } else if (ring) {
+    hipError_t e = launch_gemm_bf16_gateup(f, s);
+    if (e != hipSuccess) return e;
   } else {
     a.nb_per_tile = a.N / 64;
     long items = max_tiles * a.nb_per_tile;
@@ -502,8 +541,13 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
     long grid = items < cu * 16 ? items : cu * 16;
     k_stream_bf16<MODE_DOWN, 2><<<(unsigned)grid, 256, 0, s>>>(a);
   } else {
+    if (ring) {
+      a.tiles = f.tiles_down;
+      a.tile_count = f.tile_count + 1;
+    }
     a.nb_per_tile = a.N / 128;
-    long items = max_tiles * a.nb_per_tile;
+    const long tiles_down = ring ? G + hrows / TBM + 1 : max_tiles;
+    long items = tiles_down * a.nb_per_tile;
     long grid = items < cu * 2 ? items : cu * 2;
     k_tile_bf16<MODE_DOWN><<<(unsigned)grid, 256, 0, s>>>(a);
   }

@@ -1,0 +1,237 @@
+// Prefill-shaped grouped bf16 GEMM for the gate/up half of the expert FFN,
+// with the fused SiLU epilogue, on the packed operand layout of ffn.hip.
+//
+// Work item = (tile of <= 256 rows of one group, 128 gate + 128 up columns).
+// A workgroup of 4 wavefronts (2 x 2) computes 256 x 256 B-columns:
+// wavefront (wm, wn) owns 128 rows x 128 columns = 4 x 4 MFMA blocks of
+// 32 x 32 (256 fp32 accumulators per lane, one wavefront per SIMD).  The
+// reduction runs in 32-wide stages held in a ring of 4 LDS stages; each stage
+// is 16 A blocks + 16 B blocks of 1 KiB in lane order, filled by
+// global_load_lds_dwordx4 (each lane's 16 bytes land at block base + 16 *
+// lane, so no registers stage the copy and every fragment read is one
+// conflict-free ds_read_b128).  Loads run three stages ahead of the MFMAs;
+// one barrier per stage.
+//
+// Placement: workgroups are dealt round-robin to the 8 XCDs (workgroup b on
+// XCD b % 8).  Items are numbered column block fastest, so consecutive items
+// share their A rows; a round of the persistent loop gives each XCD a
+// contiguous run of items, so the workgroups of one XCD share one tile's A
+// rows through that XCD's L2.
+#include "common.h"
+
+namespace moe {
+
+struct GArgs {
+  const int4* tiles;
+  const int32_t* tile_count;
+  int nb_per_tile;
+  int K, N;
+  int P, cap;
+  const bf16_t* a_routed;
+  const int32_t* a_rows;
+  const bf16_t* a_shared;
+  const void* const* w0_arr;
+  const void* const* w1_arr;
+  const void* w0_sh;
+  const void* w1_sh;
+  bf16_t* h_out;
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 left at maximum).
+#define WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (0xF << 8))
+
+// Workgroup barrier for the LDS ring.  The stage about to be read was written
+// by global_load_lds (tracked by vmcnt, waited for with WAIT_VMCNT by every
+// wavefront before it arrives here); the stage about to be overwritten was
+// read into registers that the MFMAs before this point consumed (lgkmcnt is
+// drained here).  A memory-model fence would also drain the prefetches still
+// in flight, so only the compiler is fenced.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0), vmcnt/expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ f32x4_t mfma16b(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma32b(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// Workgroup = 2 x 2 wavefronts; wavefront (wm, wn) owns TM x TN blocks of
+// 32 x 32 computed with v_mfma_f32_32x32x16_bf16 (on gfx950 this instruction
+// sustains about 1.6x the rate of the 16x16x32 form), so a tile is 64*TM rows
+// x 64*TN B-columns.  Ring of 4 LDS stages of 32-wide K, each holding the
+// tile's 16 x 32 operand blocks (1 KiB, lane order) as staged by
+// global_load_lds.  A 32 x 16 MFMA operand is read from two vertically
+// adjacent blocks: lane l takes row l % 32 (block (l % 32) / 16, its row
+// l % 16) and K-slot 2s + l / 32 of the stage's 32-wide K (substep s = 0, 1):
+// 16 lanes read 256 contiguous bytes, conflict-free.  The accumulator of lane
+// l holds column l % 32 and rows 8 * (r / 4) + 4 * (l / 32) + r % 4, r < 16.
+template <int TM, int TN>
+__global__ __launch_bounds__(256) void k_gemm_bf16(GArgs a) {
+  constexpr int NA = 4 * TM, NB = 4 * TN;          // 16-wide blocks per stage
+  constexpr int HA = NA / 4, HB = NB / 4;          // DMA per wavefront
+  __shared__ u32x4_t la0[NA * 64], la1[NA * 64], la2[NA * 64], la3[NA * 64];
+  __shared__ u32x4_t lb0[NB * 64], lb1[NB * 64], lb2[NB * 64], lb3[NB * 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int c16 = lane & 15, q = lane >> 4;
+  const int c32 = lane & 31, hi = (lane >> 4) & 1, ks = lane >> 5;
+  const int K = a.K, KB = K / 32, KT = K / 32;
+  const int total = a.tile_count[0] * a.nb_per_tile;
+  const int G = gridDim.x, per_xcd = G >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  for (int base = 0; base < total; base += G) {
+    const int item = base + xcd * per_xcd + slot;
+    if (item >= total) continue;           // uniform for the workgroup
+    const int tile = item / a.nb_per_tile;
+    const int nb = item - tile * a.nb_per_tile;
+    const int4 td = a.tiles[tile];
+    const int g = td.x, row0 = td.y, nrows = td.z;
+    const bool sh = g == a.P;
+    // this wavefront stages A row blocks w + 4h and B column blocks w + 4h
+    const bf16_t* ga[HA];
+    const u32x4_t* gb[HB];
+#pragma unroll
+    for (int h = 0; h < HA; ++h) {
+      const int mb = w + 4 * h;
+      int r = mb * 16 + c16;
+      if (r >= nrows) r = 0;               // padded rows read row 0, unused
+      const int rr = row0 + r;
+      const bf16_t* rowp = sh ? a.a_shared + (size_t)rr * K
+                              : a.a_routed + (size_t)(a.a_rows ? a.a_rows[rr] : rr) * K;
+      ga[h] = rowp + 8 * q;
+    }
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      const int cb = w + 4 * h;
+      // column blocks [0, NB/2) are gate, the rest up, of the same outputs
+      const void* W = cb < NB / 2 ? (sh ? a.w0_sh : a.w0_arr[g])
+                                  : (sh ? a.w1_sh : a.w1_arr[g]);
+      const int nb16 = nb * (NB / 2) + (cb < NB / 2 ? cb : cb - NB / 2);
+      gb[h] = (const u32x4_t*)W + (size_t)nb16 * KB * 64 + lane;
+    }
+    auto issue = [&](int kt, u32x4_t* A, u32x4_t* B) {
+#pragma unroll
+      for (int h = 0; h < HA; ++h) lds_dma16(ga[h] + kt * 32, A + (w + 4 * h) * 64);
+#pragma unroll
+      for (int h = 0; h < HB; ++h) lds_dma16(gb[h] + (size_t)kt * 64, B + (w + 4 * h) * 64);
+    };
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
+    const int valid_rows = nrows - wm * TM * 32;   // may be <= 0
+    auto compute = [&](const u32x4_t* A, const u32x4_t* B) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int pos = c16 + 16 * (2 * s + ks);   // lane slot inside a block
+        u32x4_t fb[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          // 32-column block of B: j < TN/2 gate, else the matching up block
+          const int cb32 = (j < TN / 2) ? wn * (TN / 2) + j
+                                        : NB / 4 + wn * (TN / 2) + (j - TN / 2);
+          fb[j] = B[(2 * cb32 + hi) * 64 + pos];
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const u32x4_t fa = A[(2 * (wm * TM + i) + hi) * 64 + pos];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32b(fa, fb[j], acc[i][j]);
+        }
+      }
+    };
+    lds_barrier();                       // previous item done with the ring
+    // prologue: stages 0..2 (KT >= 4)
+    issue(0, la0, lb0);
+    issue(1, la1, lb1);
+    issue(2, la2, lb2);
+    // Main loop, four stages per trip (KT % 4 == 0).  Every step issues one
+    // stage (past the end it re-reads the last stage into a ring slot that is
+    // never read again), so exactly two later stages (HA + HB loads each) are
+    // in flight and "this stage has landed" is one fixed vmcnt at every step.
+    for (int kt = 0; kt < KT; kt += 4) {
+#define GEMM_STEP(S, AC, BC, AN, BN_)                          \
+      {                                                        \
+        const int k = kt + S;                                  \
+        WAIT_VMCNT(2 * (HA + HB));                             \
+        lds_barrier();                                         \
+        issue(k + 3 < KT ? k + 3 : KT - 1, AN, BN_);           \
+        if (valid_rows > 0) compute(AC, BC);                   \
+      }
+      GEMM_STEP(0, la0, lb0, la3, lb3)
+      GEMM_STEP(1, la1, lb1, la0, lb0)
+      GEMM_STEP(2, la2, lb2, la1, lb1)
+      GEMM_STEP(3, la3, lb3, la2, lb2)
+#undef GEMM_STEP
+    }
+    WAIT_VMCNT(0);                       // the trailing re-reads have landed
+    // epilogue, one row block at a time
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * TM * 32 + i * 32 + 8 * (r >> 2) + 4 * ks + (r & 3);
+        if (lr >= nrows) continue;
+        const size_t hr = (size_t)(sh ? a.cap : 0) + row0 + lr;
+#pragma unroll
+        for (int jj = 0; jj < TN / 2; ++jj) {
+          const int n = nb * (NB / 2) * 16 + (wn * (TN / 2) + jj) * 32 + c32;
+          a.h_out[hr * a.N + n] =
+              f32_to_bf16(silu_f32(acc[i][jj][r]) * acc[i][TN / 2 + jj][r]);
+        }
+      }
+    }
+  }
+}
+
+// Wavefront tile of 4 x 4 blocks of 32 x 32: 256 x 256 workgroup tiles with
+// 128 KiB of LDS (one workgroup per CU).
+static constexpr int kGemmT = 4;
+static constexpr int kGemmRows = 64 * kGemmT;
+int gemm_tile_rows() { return kGemmRows; }
+
+hipError_t launch_gemm_bf16_gateup(const FfnArgs& f, hipStream_t s) {
+  const moe_weights* w = f.w;
+  GArgs a{};
+  a.tiles = f.tiles;
+  a.tile_count = f.tile_count;
+  a.P = f.P;
+  a.cap = f.cap;
+  a.K = f.H;
+  a.N = f.I;
+  a.a_routed = (const bf16_t*)f.a_routed;
+  a.a_rows = f.a_rows;
+  a.a_shared = (const bf16_t*)f.a_shared;
+  a.w0_arr = w->w_gate;
+  a.w1_arr = w->w_up;
+  a.w0_sh = w->sh_gate;
+  a.w1_sh = w->sh_up;
+  a.h_out = (bf16_t*)f.h;
+  a.nb_per_tile = a.N / (32 * kGemmT);   // 64*T B-columns = 32*T outputs
+  // persistent: one workgroup per CU (128 KiB of LDS, 512 VGPRs a lane)
+  k_gemm_bf16<kGemmT, kGemmT><<<256, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe
