@@ -7,6 +7,12 @@ combine) over one batch of synthetic input already resident in HBM.  The
 headline workload is the decode share of a GLM-5.3-shaped layer (T=256,
 H=6144, I=2048, 32 of 256 experts local, k=8, bf16).  Prints ONE JSON line.
 
+Workloads: tiny, decode, prefill, skewed (prefill shape with a Zipf logit
+bias, identity placement), skewed_eplb (the same batch with the 8 hottest
+local experts given a second physical copy, placed from the first pass's
+expert counts by the library's moe_eplb_hottest_map; the layer then reads 40
+physical experts' weights), fp8.
+
 Besides throughput the line carries:
 * roofline: the dominant kernel's algorithmic bytes (or flops) per launch over
   its average duration, timed with HIP events recorded by the library on the
@@ -69,6 +75,18 @@ class Hip:
         self.h.hipEventDestroy(e)
 
 
+def replica_counts(local_counts, l2p, rep, P):
+    """Rows of every physical expert: replica r of an expert with n pairs and
+    R replicas gets ceil((n - r) / R) of them (pair n goes to replica n % R)."""
+    out = np.zeros(P, dtype=np.int64)
+    for e, n in enumerate(local_counts):
+        R = int(rep[e]) if rep is not None else 1
+        for r in range(R):
+            p = int(l2p[e][r]) if l2p is not None else e
+            out[p] = max(0, -(-(int(n) - r) // R))
+    return out
+
+
 def kernel_units(wl, counts, P, phys_counts):
     """Algorithmic work of the gate/up and down launches for this batch."""
     H, I = wl.H, wl.I
@@ -89,7 +107,7 @@ def kernel_units(wl, counts, P, phys_counts):
                 weight_bytes=n_w * 3 * H * I * wb)
 
 
-def cpu_baseline(wl, sample_tokens):
+def cpu_baseline(wl, sample_tokens, l2p=None, rep=None, P=None):
     """The oracle as it stands, on the host cores, over a bounded sample."""
     from oracle import moe as omoe
     try:
@@ -99,7 +117,8 @@ def cpu_baseline(wl, sample_tokens):
         threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     ex = omoe.expert_set_from_workload(wl, lazy=True)
-    res = omoe.layer_from_workload(wl, ex, token_subset=sample_tokens)
+    res = omoe.layer_from_workload(wl, ex, l2p=l2p, rep_count=rep, P=P,
+                                   token_subset=sample_tokens)
     dt = time.perf_counter() - t0
     n = len(sample_tokens)
     return res, dict(value=n / dt, unit="tokens/s", cores=int(threads),
@@ -115,7 +134,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "prefill", "skewed", "fp8"])
+                    choices=["tiny", "decode", "prefill", "skewed",
+                             "skewed_eplb", "fp8"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the CPU oracle baseline leg")
@@ -135,19 +155,44 @@ def main():
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
-    wl = make_workload(args.workload, seed=args.seed)
+    eplb = args.workload == "skewed_eplb"
+    wl = make_workload("skewed" if eplb else args.workload, seed=args.seed)
     log(f"bench: {wl.describe()}")
-    P = wl.num_local
-    prob = m.make_problem(T=wl.T, H=wl.H, I=wl.I, E=wl.E, k=wl.k,
-                          expert_begin=wl.expert_begin,
-                          num_local=wl.num_local, has_shared=wl.shared,
-                          act=wl.act, wdt=wl.wdt, out=wl.out)
     t0 = time.perf_counter()
-    dl = DeviceLayer(prob, [wl.expert(e) for e in range(wl.num_local)],
-                     wl.shared_expert)
-    b = dl.buffers()
     dlog, dx = to_dev(wl.logits), to_dev(wl.x)
     dbias = None if wl.bias is None else to_dev(wl.bias)
+    l2p = rep = None
+    P = wl.num_local
+    phys_to_logical = None
+    if eplb:
+        # expert counts of this batch (the first pass), then the placement
+        prob0 = m.make_problem(T=wl.T, H=wl.H, I=wl.I, E=wl.E, k=wl.k,
+                               expert_begin=wl.expert_begin,
+                               num_local=wl.num_local, has_shared=wl.shared,
+                               act=wl.act, wdt=wl.wdt, out=wl.out)
+        ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+        cnt = torch.zeros(wl.E, dtype=torch.int32, device="cuda")
+        L.moe_route_topk(prob0, dlog, dbias, ids, w, cnt)
+        local = cnt.cpu().numpy()[wl.expert_begin: wl.expert_begin + wl.num_local]
+        l2p, rep, P = L.moe_eplb_hottest_map(local, wl.redundant)
+        l2p = np.asarray(l2p, dtype=np.int32)
+        rep = np.asarray(rep, dtype=np.int32)
+        phys_to_logical = [-1] * P
+        for e in range(wl.num_local):
+            for r in range(int(rep[e])):
+                phys_to_logical[int(l2p[e][r])] = e
+        del ids, w, cnt
+    prob = m.make_problem(T=wl.T, H=wl.H, I=wl.I, E=wl.E, k=wl.k,
+                          expert_begin=wl.expert_begin,
+                          num_local=wl.num_local, num_physical=P,
+                          max_replicas=1 if l2p is None else int(np.shape(l2p)[1]),
+                          has_shared=wl.shared,
+                          act=wl.act, wdt=wl.wdt, out=wl.out)
+    dl = DeviceLayer(prob, [wl.expert(e) for e in range(wl.num_local)],
+                     wl.shared_expert, phys_to_logical=phys_to_logical,
+                     l2p=l2p, replica_count=rep)
+    b = dl.buffers()
     torch.cuda.synchronize()
     log(f"bench: inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
     stream = torch.cuda.current_stream().cuda_stream
@@ -178,8 +223,8 @@ def main():
     reps = max(10, min(args.steps, 50))
     evs = [[hip.event() for _ in range(L.MOE_STAGE_EVENTS)] for _ in range(reps)]
     for r in range(reps):
-        L.moe_layer_forward_timed(prob, dlog, dbias, dx, dl.weights, None,
-                                  None, b.out, b.counts, b.ws_layer,
+        L.moe_layer_forward_timed(prob, dlog, dbias, dx, dl.weights, dl.l2p,
+                                  dl.rep, b.out, b.counts, b.ws_layer,
                                   b.ws_layer.numel(), evs[r], stream=stream)
     torch.cuda.synchronize()
     stage_ms = {name: float(np.mean([hip.ms(evs[r][i], evs[r][i + 1])
@@ -190,8 +235,8 @@ def main():
             hip.destroy(e)
 
     counts = b.counts.cpu().numpy()
-    # identity replica map: physical expert e is local logical expert e
-    phys_counts = counts[wl.expert_begin: wl.expert_begin + wl.num_local]
+    local_counts = counts[wl.expert_begin: wl.expert_begin + wl.num_local]
+    phys_counts = replica_counts(local_counts, l2p, rep, P)
     u = kernel_units(wl, counts, P, phys_counts)
     tokens_per_s = wl.T / (ms_per_step * 1e-3)
     flops = u["gu_flops"] + u["dn_flops"]
@@ -218,6 +263,17 @@ def main():
                     traffic=None, algorithmic_flops=u["gu_flops"],
                     avg_us=round(gu_s * 1e6, 2))
 
+    # whole-layer roofline: the larger of the flop time at the MFMA peak and
+    # the time to move the minimum bytes (weights of non-empty experts, x,
+    # logits, out) at the HBM peak, over the measured step
+    ab = 4 if wl.act == "f32" else 2
+    ob = 4 if wl.out == "f32" else 2
+    min_bytes = (u["weight_bytes"] + wl.T * wl.H * ab + wl.T * wl.E * 4
+                 + wl.T * wl.H * ob)
+    t_flop = flops / (MFMA_PEAK_TFLOPS[prec] * 1e12)
+    t_mem = min_bytes / (HBM_PEAK_GBPS * 1e9)
+    layer_roof = max(t_flop, t_mem) / (ms_per_step * 1e-3)
+
     result = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -231,7 +287,7 @@ def main():
         "vs_baseline": None,
         "dtype": prec,
         "data": "synthetic",
-        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I,
+        "config": {"workload": args.workload, "T": wl.T, "H": wl.H, "I": wl.I,
                    "E": wl.E, "k": wl.k, "local_experts": wl.num_local,
                    "shared_expert": wl.shared, "weights": wl.wdt,
                    "activations": wl.act, "out": wl.out, "seed": wl.seed},
@@ -241,17 +297,30 @@ def main():
                   "TFLOPps": round(layer_tflops, 2),
                   "mfma_frac": round(layer_tflops / MFMA_PEAK_TFLOPS[prec], 4),
                   "local_rows": u["N"], "nonempty_experts": u["nonempty"],
-                  "expert_weight_bytes": u["weight_bytes"]},
+                  "expert_weight_bytes": u["weight_bytes"],
+                  "min_bytes": int(min_bytes),
+                  "roofline_frac": round(layer_roof, 4),
+                  "roofline_bound": "mfma" if t_flop > t_mem else "hbm"},
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "down_GBps": round(u["dn_bytes"] / dn_s / 1e9, 1),
     }
+    if wl.name == "skewed":
+        lc = local_counts.astype(np.float64)
+        pc = phys_counts.astype(np.float64)
+        result["imbalance"] = {
+            "physical_experts": P,
+            "busiest_over_mean": round(float(pc.max() / pc.mean()), 3),
+            "mean_over_busiest": round(float(pc.mean() / pc.max()), 4),
+            "busiest_over_mean_without_replicas": round(float(lc.max() / lc.mean()), 3),
+            "empty_local_experts": int(np.count_nonzero(lc == 0)),
+        }
     if not args.no_cpu:
         n = args.cpu_tokens or {"tiny": 128, "decode": 256, "prefill": 16,
                                 "skewed": 16, "fp8": 16}[wl.name]
         rng = np.random.default_rng(1)
         tok = np.sort(rng.choice(wl.T, size=min(n, wl.T), replace=False))
         log(f"bench: CPU oracle on {len(tok)} tokens ...")
-        res, base = cpu_baseline(wl, tok)
+        res, base = cpu_baseline(wl, tok, l2p, rep, P if eplb else None)
         result["cpu_baseline"] = base
         from oracle import moe as omoe
         got = b.out[: wl.T * wl.H].cpu().numpy()
@@ -259,8 +328,15 @@ def main():
                else got.astype(np.float64)).reshape(wl.T, wl.H)[tok]
         ref = res.out[tok]
         rms = float(np.sqrt(np.mean(ref * ref)))
-        result["parity_sample_max_err_over_rms"] = float(
-            np.max(np.abs(got - ref)) / rms)
+        err = np.abs(got - ref)
+        half = (omoe.bf16_half_ulp(ref) if wl.out == "bf16"
+                else omoe.f32_half_ulp(ref))
+        # the tests' measure: error beyond the output format's own rounding
+        result["parity_sample"] = {
+            "tokens": int(len(tok)),
+            "max_err_over_rms": float(np.max(err) / rms),
+            "max_err_beyond_out_rounding_over_rms": float(np.max(err - half) / rms),
+            "bar": {"f32": 1e-5, "bf16": 1e-2, "fp8": 4e-2}[prec]}
     print(json.dumps(result), flush=True)
 
 

@@ -7,7 +7,8 @@ from . import _lib  # noqa: F401
 from ._lib import (DeviceWeights, MoeError, Problem, Weights,  # noqa: F401
                    device_weights, make_problem, moe_check_problem,
                    moe_combine, moe_dispatch, moe_dispatch_workspace_size,
-                   moe_eplb_hottest_map, moe_ffn_workspace_size,
+                   moe_eplb_hottest_map, moe_eplb_plan, moe_eplb_rank_map,
+                   moe_eplb_record_load, moe_ffn_workspace_size,
                    moe_grouped_ffn, moe_layer_forward,
                    moe_layer_workspace_size, moe_quantize_fp8_blocks,
                    moe_prepack_weights, moe_route_topk, status_string)

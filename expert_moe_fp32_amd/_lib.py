@@ -27,7 +27,8 @@ EXPORTS = (
     "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
     "moe_layer_forward_timed", "moe_prepack_weights",
     "moe_quantize_fp8_blocks",
-    "moe_eplb_hottest_map",
+    "moe_eplb_hottest_map", "moe_eplb_plan", "moe_eplb_rank_map",
+    "moe_eplb_record_load",
 )
 MOE_STAGE_EVENTS = 8
 STAGES = ("route", "dispatch_index", "gather", "tiles", "gate_up", "down",
@@ -91,6 +92,11 @@ def lib() -> ctypes.CDLL:
             "moe_quantize_fp8_blocks": (ctypes.c_int, [V, I32, I32, I32, V, V,
                                                        V]),
             "moe_eplb_hottest_map": (ctypes.c_int, [V, I32, I32, V, V, V]),
+            "moe_eplb_plan": (ctypes.c_int, [V, I32, I32, I32, V, V, V, V]),
+            "moe_eplb_rank_map": (ctypes.c_int, [V, V, V, I32, I32, I32, I32,
+                                                 I32, V, V, V]),
+            "moe_eplb_record_load": (ctypes.c_int, [V, I32, I32,
+                                                    ctypes.c_int64, V, V, V]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -269,6 +275,57 @@ def moe_eplb_hottest_map(local_counts: Sequence[int], redundant: int):
            "moe_eplb_hottest_map")
     return ([[l2p[2 * e], l2p[2 * e + 1]] for e in range(L)], list(rep),
             P.value)
+
+
+def moe_eplb_plan(load: Sequence[int], ep: int, redundant: int):
+    """Group-wide replica plan and placement (host).  Returns (replicas [E],
+    slot_expert [ep][S], slot_replica [ep][S], rank_load [ep]) as lists."""
+    E = len(load)
+    if E < 1 or ep < 1 or (E + redundant) % ep:
+        raise MoeError(MOE_ERR_INVALID_ARGUMENT, "moe_eplb_plan")
+    S = (E + redundant) // ep
+    ld = (ctypes.c_int64 * E)(*[int(v) for v in load])
+    rep = (ctypes.c_int32 * E)()
+    se = (ctypes.c_int32 * (ep * S))()
+    sr = (ctypes.c_int32 * (ep * S))()
+    rl = (ctypes.c_double * ep)()
+    _check(lib().moe_eplb_plan(ctypes.addressof(ld), E, ep, redundant,
+                               ctypes.addressof(rep), ctypes.addressof(se),
+                               ctypes.addressof(sr), ctypes.addressof(rl)),
+           "moe_eplb_plan")
+    return (list(rep), [list(se[g * S:(g + 1) * S]) for g in range(ep)],
+            [list(sr[g * S:(g + 1) * S]) for g in range(ep)], list(rl))
+
+
+def moe_eplb_rank_map(replicas, slot_expert, slot_replica, redundant: int,
+                      rank: int, max_replicas: Optional[int] = None):
+    """One rank's (l2p [E][max_replicas], replica_count [E], P) from a plan."""
+    E, ep = len(replicas), len(slot_expert)
+    S = len(slot_expert[0]) if ep else 0
+    mr = max(replicas) if max_replicas is None else max_replicas
+    rep = (ctypes.c_int32 * E)(*replicas)
+    se = (ctypes.c_int32 * (ep * S))(*[v for row in slot_expert for v in row])
+    sr = (ctypes.c_int32 * (ep * S))(*[v for row in slot_replica for v in row])
+    l2p = (ctypes.c_int32 * (E * mr))()
+    rc = (ctypes.c_int32 * E)()
+    P = ctypes.c_int32(0)
+    _check(lib().moe_eplb_rank_map(ctypes.addressof(rep), ctypes.addressof(se),
+                                   ctypes.addressof(sr), E, ep, redundant,
+                                   rank, mr, ctypes.addressof(l2p),
+                                   ctypes.addressof(rc), ctypes.addressof(P)),
+           "moe_eplb_rank_map")
+    return ([list(l2p[e * mr:(e + 1) * mr]) for e in range(E)], list(rc),
+            P.value)
+
+
+def moe_eplb_record_load(expert_counts, E: int, window: int, step: int,
+                         history, window_load, stream=None) -> None:
+    """Device sliding-window load record (see include/moe.h)."""
+    _check(lib().moe_eplb_record_load(ptr(expert_counts), E, window, step,
+                                      ptr(history), ptr(window_load),
+                                      current_stream() if stream is None
+                                      else stream),
+           "moe_eplb_record_load")
 
 
 # ------------------------------------------------- device weight plumbing

@@ -90,9 +90,13 @@ bool ffn_built(const moe_problem* p) {
   return p != nullptr;
 }
 
+// Expected rows per physical expert: the local pairs over the physical
+// experts, where a rank with fewer physical than logical experts (a
+// group-wide placement whose other replicas sit on other ranks) expects
+// about one logical expert's pairs per physical expert.
 int rows_hint(const moe_problem* p) {
   const double pairs = (double)p->T * p->k * p->num_local / p->E;
-  return (int)(pairs / p->num_physical + 0.5);
+  return (int)(pairs / std::max(p->num_physical, p->num_local) + 0.5);
 }
 
 moe_status launch_ffn_common(const moe_problem* p, const void* x_perm,
@@ -227,7 +231,7 @@ moe_status moe_check_problem(const moe_problem* p) {
   if (p->expert_begin < 0 || p->num_local < 1 ||
       (long)p->expert_begin + p->num_local > p->E)
     return MOE_ERR_INVALID_ARGUMENT;
-  if (p->num_physical < p->num_local || p->max_replicas < 1)
+  if (p->num_physical < 1 || p->max_replicas < 1)
     return MOE_ERR_INVALID_ARGUMENT;
   if (p->has_shared != 0 && p->has_shared != 1) return MOE_ERR_INVALID_ARGUMENT;
   const int a = p->act_dtype, w = p->weight_dtype, o = p->out_dtype;
@@ -519,34 +523,6 @@ moe_status moe_quantize_fp8_blocks(const float* w, int32_t rows, int32_t cols,
   if (rows == 0 || cols == 0) return MOE_OK;
   if (!w || !codes || !scales) return MOE_ERR_INVALID_ARGUMENT;
   return hip_status(launch_quant_blocks_fp8(w, rows, cols, codes, scales, S(stream)));
-}
-
-moe_status moe_eplb_hottest_map(const int32_t* local_counts, int32_t num_local,
-                                int32_t redundant, int32_t* l2p,
-                                int32_t* replica_count,
-                                int32_t* num_physical) {
-  if (!local_counts || !l2p || !replica_count || !num_physical)
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (num_local < 1 || num_local > MOE_LMAX || redundant < 0 ||
-      redundant > num_local || num_local + redundant > MOE_LMAX)
-    return MOE_ERR_INVALID_ARGUMENT;
-  std::vector<int> order(num_local);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
-    return local_counts[a] > local_counts[b];
-  });
-  for (int e = 0; e < num_local; ++e) {
-    l2p[2 * e] = e;
-    l2p[2 * e + 1] = -1;
-    replica_count[e] = 1;
-  }
-  for (int i = 0; i < redundant; ++i) {
-    const int e = order[i];
-    l2p[2 * e + 1] = num_local + i;
-    replica_count[e] = 2;
-  }
-  *num_physical = num_local + redundant;
-  return MOE_OK;
 }
 
 }  // extern "C"

@@ -29,8 +29,8 @@
  *  - Errors are reported only through the returned status; nothing is
  *    printed and nothing aborts.  Argument errors are detected on the host
  *    before any work is enqueued.  Device-data preconditions (finite logits;
- *    map entries in [0, P); each physical id used by exactly one (expert,
- *    replica)) are not checked.
+ *    map entries in [0, P) or -1; each physical id used by exactly one
+ *    (expert, replica)) are not checked.
  *  - T = 0 is valid: the call enqueues nothing and succeeds (an idle rank's
  *    dummy forward, infra-guide page, section 4.3).
  *  - Re-entrant; no global mutable state.
@@ -75,7 +75,8 @@ typedef struct {
   int32_t k;            /* experts per token, 1 <= k <= E                    */
   int32_t expert_begin; /* this rank owns logical experts                    */
   int32_t num_local;    /*   [expert_begin, expert_begin + num_local)        */
-  int32_t num_physical; /* P >= num_local physical experts (with replicas)  */
+  int32_t num_physical; /* P >= 1 physical experts held here: num_local plus
+                           local replicas, or a group-wide placement's S */
   int32_t max_replicas; /* columns of the logical-to-physical map (>= 1)     */
   int32_t has_shared;   /* 1: one always-on shared expert, weight 1          */
   int32_t act_dtype;    /* moe_dtype of x                                    */
@@ -145,7 +146,10 @@ MOE_API moe_status moe_route_topk(const moe_problem* p, const float* logits,
  *   topk_ids/_w   from moe_route_topk
  *   l2p           [num_local][max_replicas] int32 logical-to-physical map;
  *                 column r < replica_count[e] holds the physical id of
- *                 replica r of local expert e.  NULL = identity (P must equal
+ *                 replica r of local expert e, or -1 when that replica is
+ *                 placed on another rank (section 5.2's placement spreads an
+ *                 expert's replicas over cards): such pairs count in n below
+ *                 but are not local here.  NULL = identity (P must equal
  *                 num_local and replica_count must be NULL).
  *   replica_count [num_local] int32, each in [1, max_replicas], or NULL
  * A local pair is (t, j) with topk_ids[t][j] in the rank's range.  Walking
@@ -268,6 +272,62 @@ MOE_API moe_status moe_eplb_hottest_map(const int32_t* local_counts,
                                 int32_t num_local, int32_t redundant,
                                 int32_t* l2p, int32_t* replica_count,
                                 int32_t* num_physical);
+
+/* Replica plan and placement over an EP group (infra-guide page, section
+ * 5.2: redundant slots go one at a time to the expert with the highest load
+ * per replica; replicas are then placed heaviest first onto the currently
+ * lightest rank that still has a free slot; section 5.3: every rank holds
+ * (E + redundant) / ep physical experts).  All arrays are HOST memory.
+ *   load         [E] int64 load per logical expert (e.g. a window sum from
+ *                moe_eplb_record_load), each >= 0
+ *   replicas     [E] out: replica count per expert (sums to E + redundant)
+ *   slot_expert  [ep][S] out, S = (E + redundant) / ep: rank g's physical
+ *                expert s is a replica of expert slot_expert[g][s]; a rank's
+ *                slots are in (expert, replica) order
+ *   slot_replica [ep][S] out: which replica of that expert
+ *   rank_load    [ep] out: sum over the rank's replicas of load / replicas,
+ *                added in placement order
+ * Ties: the lower expert id gets a redundant slot; equal per-replica loads
+ * are placed in (expert, replica) order; the lower rank wins among equally
+ * light ranks.  INVALID_ARGUMENT when (E + redundant) % ep != 0 or a load
+ * is negative. */
+MOE_API moe_status moe_eplb_plan(const int64_t* load, int32_t E, int32_t ep,
+                         int32_t redundant, int32_t* replicas,
+                         int32_t* slot_expert, int32_t* slot_replica,
+                         double* rank_load);
+
+/* One rank's dispatch map under a plan from moe_eplb_plan, for a problem
+ * with expert_begin = 0, num_local = E, num_physical = S and max_replicas
+ * columns.  All arrays are HOST memory.
+ *   l2p           [E][max_replicas] out: physical id on this rank of replica
+ *                 r of expert e, -1 when it is placed on another rank
+ *   replica_count [E] out: the expert's replica count over the whole group
+ *   num_physical  out: S
+ * INVALID_ARGUMENT when a replica count exceeds max_replicas or the plan's
+ * entries are out of range. */
+MOE_API moe_status moe_eplb_rank_map(const int32_t* replicas,
+                             const int32_t* slot_expert,
+                             const int32_t* slot_replica, int32_t E,
+                             int32_t ep, int32_t redundant, int32_t rank,
+                             int32_t max_replicas, int32_t* l2p,
+                             int32_t* replica_count, int32_t* num_physical);
+
+/* Sliding-window load record (section 5.3: the balancer records per-expert
+ * load every forward and plans from the most recent window of steps).
+ * Enqueued on `stream`; no synchronisation.
+ *   expert_counts [E] int32 device: this step's pairs per expert (the
+ *                 expert_counts output of moe_route_topk/moe_layer_forward)
+ *   history       [window][E] int32 device ring, zeroed by the caller
+ *                 before step 0
+ *   window_load   [E] int64 device, zeroed with the history: after the call
+ *                 for step s it holds the sum of the counts of steps
+ *                 max(0, s - window + 1) .. s
+ * Calls must come in step order 0, 1, 2, ... on one stream; step selects the
+ * ring slot step % window. */
+MOE_API moe_status moe_eplb_record_load(const int32_t* expert_counts,
+                                int32_t E, int32_t window, int64_t step,
+                                int32_t* history, int64_t* window_load,
+                                void* stream);
 
 #ifdef __cplusplus
 }

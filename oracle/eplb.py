@@ -126,6 +126,33 @@ def place_replicas(counts: Sequence[int], replicas: Sequence[int], ep: int
     return held, load
 
 
+def rank_map(held: Sequence[Sequence[Tuple[int, int]]],
+             replicas: Sequence[int], rank: int):
+    """Dispatch map of one rank under a placement over all ranks.
+
+    The rank's physical experts are its slots ordered by (expert, replica);
+    l2p[e, r] is the physical id on this rank of replica r of expert e, or -1
+    when that replica is placed on another rank; rep_count[e] is the
+    expert's replica count over the whole group, so pair n of e still goes to
+    replica n mod R_e.  Returns (l2p [E, max(replicas)], rep_count [E], P)."""
+    E = len(replicas)
+    slots = sorted(held[rank])
+    l2p = np.full((E, max(replicas)), -1, dtype=np.int32)
+    for pid, (e, r) in enumerate(slots):
+        l2p[e, r] = pid
+    return l2p, np.asarray(replicas, dtype=np.int32), len(slots)
+
+
+def window_load(history: Sequence[Sequence[int]], window: int) -> np.ndarray:
+    """Load over the sliding window (section 5.3: the balancer averages the
+    recorded per-expert load over the most recent steps): the element-wise
+    sum of the last ``window`` recorded count vectors."""
+    recent = list(history)[-window:] if window > 0 else []
+    if not recent:
+        return np.zeros(0, dtype=np.int64)
+    return np.sum(np.asarray(recent, dtype=np.int64), axis=0)
+
+
 def busiest_over_mean(load: Sequence[float]) -> float:
     return max(load) / (sum(load) / len(load))
 

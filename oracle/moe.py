@@ -124,7 +124,12 @@ def dispatch(ids: np.ndarray, expert_begin: int, num_local: int,
     token picks an expert at most once), the n-th pair of local logical expert
     e goes to physical expert l2p[e, n mod R_e] at position floor(n / R_e) of
     that physical expert's segment.  Segments are concatenated in physical-id
-    order."""
+    order.
+
+    Under a placement spread over several ranks (section 5.2 of the
+    infra-guide page: replicas of one expert may sit on different cards) an
+    entry l2p[e, r] = -1 says that replica r of e lives on another rank: the
+    pair still counts in e's n, but it is not local here (pair_row -1)."""
     T, k = ids.shape
     rep_count = np.asarray(rep_count)
     n_seen = np.zeros(num_local, dtype=np.int64)
@@ -138,6 +143,8 @@ def dispatch(ids: np.ndarray, expert_begin: int, num_local: int,
                 n_seen[e] += 1
                 R = int(rep_count[e])
                 p = int(l2p[e, n % R])
+                if p == -1:                 # that replica is on another rank
+                    continue
                 if not 0 <= p < P:
                     raise ValueError("physical id out of range")
                 pair_phys[t, j] = p
@@ -318,7 +325,8 @@ def layer_forward(logits, bias, x_stored, act: str, k: int, expert_begin: int,
     phys_to_logical = np.full(P, -1, dtype=np.int64)
     for e in range(num_local):
         for r in range(int(rep_count[e])):
-            phys_to_logical[l2p[e, r]] = e
+            if l2p[e, r] != -1:          # -1: that replica is on another rank
+                phys_to_logical[l2p[e, r]] = e
     x_rows = activation_rows(x_stored, act, experts.fmt, experts.quant_block)
     hr = h_rounder(experts.fmt, act, experts.quant_block)
     want = np.ones(T, dtype=bool)

@@ -47,7 +47,8 @@ def phys_to_logical_from_map(l2p, rep, P):
     out = [-1] * P
     for e in range(len(rep)):
         for r in range(int(rep[e])):
-            out[int(l2p[e][r])] = e
+            if int(l2p[e][r]) >= 0:      # -1: replica placed on another rank
+                out[int(l2p[e][r])] = e
     return out
 
 

@@ -51,7 +51,8 @@ def good(**kw):
     (dict(k=20, E=16), L.MOE_ERR_INVALID_ARGUMENT),
     (dict(expert_begin=10), L.MOE_ERR_INVALID_ARGUMENT),
     (dict(num_local=0), L.MOE_ERR_INVALID_ARGUMENT),
-    (dict(num_physical=7), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(num_physical=0), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(num_physical=3), L.MOE_OK),          # group-wide placement share
     (dict(H=200), L.MOE_ERR_UNSUPPORTED),
     (dict(I=96), L.MOE_ERR_UNSUPPORTED),
     (dict(act="f32"), L.MOE_ERR_UNSUPPORTED),
