@@ -325,11 +325,11 @@ moe_status moe_route_topk(const moe_problem* p, const float* logits,
                           int32_t* expert_counts, void* stream) {
   moe_status st = moe_check_problem(p);
   if (st != MOE_OK) return st;
-  if (expert_counts) {
-    if (launch_fill_i32(expert_counts, 0, (size_t)p->E, S(stream)) != hipSuccess)
-      return MOE_ERR_HIP;
+  if (p->T == 0) {
+    if (expert_counts)
+      return hip_status(launch_fill_i32(expert_counts, 0, (size_t)p->E, S(stream)));
+    return MOE_OK;
   }
-  if (p->T == 0) return MOE_OK;
   if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
   return hip_status(launch_route_topk(logits, bias, p->T, p->E, p->k, topk_ids,
                                       topk_w, expert_counts, S(stream)));
@@ -443,9 +443,8 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
     extras.BM = ffn_tile_rows(p->act_dtype, p->weight_dtype, rows_hint(p),
                               p->H, &extras.balanced);
     extras.has_shared = p->has_shared;
-  } else if (launch_fill_i32(counts, 0, (size_t)p->E, s) != hipSuccess) {
-    return MOE_ERR_HIP;
   }
+  // the router's count pass stores every entry of counts (no zero fill)
   if (launch_route_topk(logits, bias, p->T, p->E, p->k, L.ids, L.tw,
                         small ? nullptr : counts, s) != hipSuccess)
     return MOE_ERR_HIP;
