@@ -335,6 +335,9 @@ moe_status moe_route_topk(const moe_problem* p, const float* logits,
                                       topk_w, expert_counts, S(stream)));
 }
 
+// 16-byte vector loads and stores touch the row arrays
+static inline bool al16(const void* q) { return ((uintptr_t)q & 15) == 0; }
+
 static moe_status check_map(const moe_problem* p, const int32_t* l2p,
                             const int32_t* rep) {
   if (!l2p) {
@@ -360,6 +363,7 @@ moe_status moe_dispatch(const moe_problem* p, const void* x,
       !row_weight || !pair_row)
     return MOE_ERR_INVALID_ARGUMENT;
   if (p->weight_dtype == MOE_FP8_E4M3 && !x_perm_scales) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al16(x) || !al16(x_perm)) return MOE_ERR_INVALID_ARGUMENT;
   size_t need;
   moe_dispatch_workspace_size(p, &need);
   if (need && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
@@ -386,6 +390,8 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm,
   if (fp8 && !x_perm_scales) return MOE_ERR_INVALID_ARGUMENT;
   if (p->has_shared && (!x_shared || !y_shared || (fp8 && !x_shared_scales)))
     return MOE_ERR_INVALID_ARGUMENT;
+  if (!al16(x_perm) || !al16(x_shared) || !al16(y_perm) || !al16(y_shared))
+    return MOE_ERR_INVALID_ARGUMENT;
   size_t need;
   moe_ffn_workspace_size(p, &need);
   if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
@@ -402,6 +408,7 @@ moe_status moe_combine(const moe_problem* p, const float* y_perm,
   if (st != MOE_OK) return st;
   if (p->T == 0) return MOE_OK;
   if (!y_perm || !pair_row || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al16(y_perm) || !al16(y_shared) || !al16(out)) return MOE_ERR_INVALID_ARGUMENT;
   return hip_status(launch_combine(y_perm, pair_row, topk_w, y_shared, p->T,
                                    p->H, p->k, p->out_dtype, out, S(stream)));
 }
@@ -424,6 +431,7 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
     return MOE_OK;
   }
   if (!logits || !x || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al16(x) || !al16(out)) return MOE_ERR_INVALID_ARGUMENT;
   size_t need;
   moe_layer_workspace_size(p, &need);
   if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;

@@ -30,6 +30,19 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 }
 
 // Each thread loads its token's local expert ids (-1 where not local).
+// Exclusive prefix sum over the 64 lanes of a wavefront; *total gets the sum.
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+  const int lane = threadIdx.x & 63;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  *total = __shfl(incl, 63, 64);
+  return incl - v;
+}
+
 __device__ __forceinline__ void load_local_ids(const int32_t* ids, int t,
                                                int T, int k, int e0, int L,
                                                int (&le)[MOE_KMAX]) {
@@ -43,6 +56,44 @@ __device__ __forceinline__ void load_local_ids(const int32_t* ids, int t,
   }
 }
 
+// For every local expert e < L, in ascending e, calls sink(e, m) on all lanes
+// with m = the ballot of the lanes whose token picked e (a token picks an
+// expert at most once).  With L <= 256 each lane first folds its picks into
+// a 256-bit mask, so an expert costs one shift-and-ballot; beyond that every
+// expert is compared against every slot.
+template <class Sink>
+__device__ __forceinline__ void for_each_expert_ballot(
+    const int (&le)[MOE_KMAX], int L, Sink sink) {
+  if (L <= 256) {
+    uint64_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_KMAX; ++j) {
+      const int e = le[j];
+      const uint64_t bit = e >= 0 ? 1ull << (e & 63) : 0ull;
+      const int w = e >> 6;
+      m0 |= w == 0 ? bit : 0ull;
+      m1 |= w == 1 ? bit : 0ull;
+      m2 |= w == 2 ? bit : 0ull;
+      m3 |= w == 3 ? bit : 0ull;
+    }
+    auto word = [&](uint64_t mw, int base) {
+      const int n = min(64, L - base);
+      for (int b = 0; b < n; ++b) sink(base + b, __ballot((mw >> b) & 1ull));
+    };
+    word(m0, 0);
+    if (L > 64) word(m1, 64);
+    if (L > 128) word(m2, 128);
+    if (L > 192) word(m3, 192);
+  } else {
+    for (int e = 0; e < L; ++e) {
+      bool has = false;
+#pragma unroll
+      for (int j = 0; j < MOE_KMAX; ++j) has |= le[j] == e;
+      sink(e, __ballot(has));
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_local_hist(
     const int32_t* __restrict__ ids, int T, int k, int e0, int L,
     int32_t* __restrict__ block_counts) {
@@ -51,20 +102,9 @@ __global__ __launch_bounds__(256) void k_local_hist(
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int le[MOE_KMAX];
   load_local_ids(ids, t, T, k, e0, L, le);
-  bool any_local = false;
-#pragma unroll
-  for (int j = 0; j < MOE_KMAX; ++j) any_local |= le[j] >= 0;
-  const bool wave_has = __ballot(any_local) != 0ull;
-  for (int e = 0; e < L; ++e) {
-    int c = 0;
-    if (wave_has) {
-      bool has = false;
-#pragma unroll
-      for (int j = 0; j < MOE_KMAX; ++j) has |= le[j] == e;
-      c = __popcll(__ballot(has));
-    }
-    if (lane == 0) wave_cnt[wv * L + e] = c;
-  }
+  for_each_expert_ballot(le, L, [&](int e, uint64_t m) {
+    if (lane == 0) wave_cnt[wv * L + e] = __popcll(m);
+  });
   __syncthreads();
   for (int e = threadIdx.x; e < L; e += blockDim.x)
     block_counts[(size_t)blockIdx.x * L + e] =
@@ -93,13 +133,16 @@ __global__ __launch_bounds__(1024) void k_scan(
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int p = 0; p < P; ++p) {
-      offsets[p] = run;
-      run += pc[p];
+  if (threadIdx.x < 64) {                  // one wavefront scans pc
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base <= P; base += 64) {
+      const int p = base + lane;
+      int tot;
+      const int ex = wave_excl_scan(p < P ? pc[p] : 0, &tot);
+      if (p <= P) offsets[p] = carry + ex;
+      carry += tot;
     }
-    offsets[P] = run;
   }
 }
 
@@ -109,36 +152,22 @@ __global__ __launch_bounds__(256) void k_permute(
     const int32_t* __restrict__ rep, const int32_t* __restrict__ block_base,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
     float* __restrict__ row_weight, int32_t* __restrict__ pair_row) {
-  extern __shared__ int32_t wave_cnt[];     // [4][L]
+  extern __shared__ uint64_t dyn[];        // bal [4][L], then wave_cnt [4][L]
+  uint64_t* bal = dyn;
+  int32_t* wave_cnt = (int32_t*)(dyn + 4 * L);
   const int t = blockIdx.x * kTokPerBlock + threadIdx.x;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int le[MOE_KMAX], rank[MOE_KMAX];
+  int le[MOE_KMAX];
   load_local_ids(ids, t, T, k, e0, L, le);
-  bool any_local = false;
-#pragma unroll
-  for (int j = 0; j < MOE_KMAX; ++j) {
-    rank[j] = 0;
-    any_local |= le[j] >= 0;
-  }
-  const bool wave_has = __ballot(any_local) != 0ull;
-  const uint64_t lt = lanemask_lt();
-  for (int e = 0; e < L; ++e) {
-    int c = 0;
-    if (wave_has) {
-      bool has = false;
-#pragma unroll
-      for (int j = 0; j < MOE_KMAX; ++j) has |= le[j] == e;
-      const uint64_t m = __ballot(has);
-      c = __popcll(m);
-      const int below = __popcll(m & lt);
-#pragma unroll
-      for (int j = 0; j < MOE_KMAX; ++j)
-        if (le[j] == e) rank[j] = below;
+  for_each_expert_ballot(le, L, [&](int e, uint64_t m) {
+    if (lane == 0) {
+      bal[wv * L + e] = m;
+      wave_cnt[wv * L + e] = __popcll(m);
     }
-    if (lane == 0) wave_cnt[wv * L + e] = c;
-  }
+  });
   __syncthreads();
   if (t >= T) return;
+  const uint64_t lt = lanemask_lt();
 #pragma unroll
   for (int j = 0; j < MOE_KMAX; ++j) {
     if (j >= k) break;
@@ -148,7 +177,8 @@ __global__ __launch_bounds__(256) void k_permute(
       pair_row[o] = -1;
       continue;
     }
-    int n = block_base[(size_t)blockIdx.x * L + e] + rank[j];
+    int n = block_base[(size_t)blockIdx.x * L + e] +
+            __popcll(bal[wv * L + e] & lt);  // earlier lanes of this wave
     for (int v = 0; v < wv; ++v) n += wave_cnt[v * L + e];
     const int R = rep ? min(max(rep[e], 1), max_rep) : 1;
     const int p = l2p ? l2p[e * max_rep + (n % R)] : e;
@@ -181,44 +211,30 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
   __shared__ int32_t pc[MOE_LMAX + 1];
   __shared__ int32_t tb[MOE_LMAX + 2];
   __shared__ int32_t wpre[16 * kSmallL];
+  __shared__ uint64_t bal[16 * kSmallL];    // per wavefront: ballot per expert
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   const int T = a.T, k = a.k, L = a.num_local, P = a.P;
   for (int i = t; i < x.E; i += 1024) cnt[i] = 0;
   for (int i = t; i <= P; i += 1024) pc[i] = 0;
   __syncthreads();
-  int le[MOE_KMAX], rank[MOE_KMAX];
-  bool any_local = false;
+  int le[MOE_KMAX];
 #pragma unroll
   for (int j = 0; j < MOE_KMAX; ++j) {
     le[j] = -1;
-    rank[j] = 0;
     if (j < k && t < T) {
       const int gid = a.ids[(size_t)t * k + j];
       atomicAdd(&cnt[gid], 1);
       const int e = gid - a.expert_begin;
-      if (e >= 0 && e < L) {
-        le[j] = e;
-        any_local = true;
-      }
+      if (e >= 0 && e < L) le[j] = e;
     }
   }
-  const bool wave_has = __ballot(any_local) != 0ull;
   const uint64_t lt = lanemask_lt();
-  for (int e = 0; e < L; ++e) {
-    int c = 0;
-    if (wave_has) {
-      bool has = false;
-#pragma unroll
-      for (int j = 0; j < MOE_KMAX; ++j) has |= le[j] == e;
-      const uint64_t m = __ballot(has);
-      c = __popcll(m);
-      const int below = __popcll(m & lt);
-#pragma unroll
-      for (int j = 0; j < MOE_KMAX; ++j)
-        if (le[j] == e) rank[j] = below;
+  for_each_expert_ballot(le, L, [&](int e, uint64_t m) {
+    if (lane == 0) {
+      bal[wv * kSmallL + e] = m;
+      wpre[wv * kSmallL + e] = __popcll(m);
     }
-    if (lane == 0) wpre[wv * kSmallL + e] = c;
-  }
+  });
   __syncthreads();
   if (x.counts)
     for (int i = t; i < x.E; i += 1024) x.counts[i] = cnt[i];
@@ -237,27 +253,41 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
     }
   }
   __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int p = 0; p < P; ++p) {
-      const int c = pc[p];
-      pc[p] = run;
-      a.offsets[p] = run;
-      run += c;
+  if (wv == 0) {
+    // segment offsets: exclusive scan of the rows per physical expert,
+    // 64 entries at a time (pc[p] becomes offsets[p] in place; pc[P] = N)
+    int carry = 0;
+    for (int base = 0; base <= P; base += 64) {
+      const int p = base + lane;
+      const int c = p < P ? pc[p] : 0;
+      int tot;
+      const int ex = wave_excl_scan(c, &tot);
+      if (p <= P) {
+        pc[p] = carry + ex;
+        a.offsets[p] = carry + ex;
+      }
+      carry += tot;
     }
-    pc[P] = run;
-    a.offsets[P] = run;
     if (x.tiles) {                         // tile list of the expert FFN
       const int G = P + (x.has_shared ? 1 : 0);
-      int nt = 0;
-      for (int g = 0; g < G; ++g) {
-        tb[g] = nt;
-        const int rows = g < P ? pc[g + 1] - pc[g] : T;
-        int per;
-        nt += tile_split(rows, x.BM, x.balanced, &per);
+      int nt_carry = 0;
+      for (int base = 0; base < G; base += 64) {
+        const int g = base + lane;
+        int nt = 0;
+        if (g < G) {
+          const int rows = g < P ? pc[g + 1] - pc[g] : T;
+          int per;
+          nt = tile_split(rows, x.BM, x.balanced, &per);
+        }
+        int tot;
+        const int ex = wave_excl_scan(nt, &tot);
+        if (g < G) tb[g] = nt_carry + ex;
+        nt_carry += tot;
       }
-      tb[G] = nt;
-      x.tile_count[0] = nt;
+      if (lane == 0) {
+        tb[G] = nt_carry;
+        x.tile_count[0] = nt_carry;
+      }
     }
   }
   __syncthreads();
@@ -284,7 +314,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
       a.pair_row[o] = -1;
       continue;
     }
-    const int n = wpre[wv * kSmallL + e] + rank[j];
+    const int n = wpre[wv * kSmallL + e] + __popcll(bal[wv * kSmallL + e] & lt);
     const int R = a.rep ? min(max(a.rep[e], 1), a.max_rep) : 1;
     const int p = a.l2p ? a.l2p[e * a.max_rep + (n % R)] : e;
     if (p < 0 || p >= P) {
@@ -311,7 +341,8 @@ hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s) {
                                       a.num_local, a.block_counts);
   k_scan<<<1, 1024, 0, s>>>(a.block_counts, nblk, a.num_local, a.P,
                             a.max_rep, a.l2p, a.rep, a.block_base, a.offsets);
-  k_permute<<<nblk, 256, lds, s>>>(a.ids, a.w, a.T, a.k, a.expert_begin,
+  const size_t lds_perm = (sizeof(uint64_t) + sizeof(int32_t)) * 4 * a.num_local;
+  k_permute<<<nblk, 256, lds_perm, s>>>(a.ids, a.w, a.T, a.k, a.expert_begin,
                                    a.num_local, a.P, a.max_rep, a.l2p, a.rep,
                                    a.block_base, a.offsets, a.row_token,
                                    a.row_weight, a.pair_row);
@@ -375,35 +406,53 @@ hipError_t launch_gather_rows_words(const void* x, int row_words,
 // ----------------------------------------------------- FP8 quantisation
 // One wavefront per (token, 128-channel group): amax over the group, scale
 // amax/448 (1 if amax = 0), codes RNE(fl32(x / scale)) saturated.
+// Per-token, per-128-channel E4M3 quantisation: a lane takes 8 consecutive
+// channels (one 16-byte load), the 16 lanes of a DPP row one 128-channel
+// group, whose amax is a 4-step row rotation.
+__device__ __forceinline__ float row_max_f32(float v) {
+#define ROWF(ctrl)                                                            \
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(                    \
+                   0, __float_as_int(v), ctrl, 0xF, 0xF, false)));
+  ROWF(0x128) ROWF(0x124) ROWF(0x122) ROWF(0x121)
+#undef ROWF
+  return v;
+}
+
 __global__ __launch_bounds__(256) void k_quant_rows_fp8(
-    const bf16_t* __restrict__ x, int T, int H, uint8_t* __restrict__ codes,
+    const bf16_t* __restrict__ x, long n8, uint8_t* __restrict__ codes,
     float* __restrict__ scales) {
-  const int G = H / 128;
-  const long grp = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (grp >= (long)T * G) return;
-  const long t = grp / G, g = grp % G;
-  const bf16_t* src = x + t * H + g * 128;
-  const uint32_t pair = *(const uint32_t*)(src + 2 * lane);
-  const float v0 = bf16_to_f32((bf16_t)(pair & 0xFFFFu));
-  const float v1 = bf16_to_f32((bf16_t)(pair >> 16));
-  float amax = fmaxf(fabsf(v0), fabsf(v1));
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;   // chunk of 8 values
+  const bool valid = i < n8;               // whole rows of 16 lanes agree
+  u32x4_t raw = {0u, 0u, 0u, 0u};
+  if (valid) raw = *(const u32x4_t*)(x + 8 * i);
+  float v[8];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = bf16_to_f32((bf16_t)(raw[q] & 0xFFFFu));
+    v[2 * q + 1] = bf16_to_f32((bf16_t)(raw[q] >> 16));
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+  amax = row_max_f32(amax);
   const float sc = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
-  const uint8_t c0 = f32_to_e4m3(__fdiv_rn(v0, sc));
-  const uint8_t c1 = f32_to_e4m3(__fdiv_rn(v1, sc));
-  *(uint16_t*)(codes + t * H + g * 128 + 2 * lane) =
-      (uint16_t)c0 | ((uint16_t)c1 << 8);
-  if (lane == 0) scales[t * G + g] = sc;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    lo |= (uint32_t)f32_to_e4m3(__fdiv_rn(v[q], sc)) << (8 * q);
+    hi |= (uint32_t)f32_to_e4m3(__fdiv_rn(v[q + 4], sc)) << (8 * q);
+  }
+  if (!valid) return;
+  *(uint2*)(codes + 8 * i) = make_uint2(lo, hi);
+  if ((threadIdx.x & 15) == 0) scales[i >> 4] = sc;
 }
 
 hipError_t launch_quant_rows_fp8(const bf16_t* x, int T, int H,
                                  uint8_t* codes, float* scales,
                                  hipStream_t s) {
-  const long groups = (long)T * (H / 128);
-  if (groups == 0) return hipSuccess;
-  k_quant_rows_fp8<<<(unsigned)((groups + 3) / 4), 256, 0, s>>>(x, T, H, codes,
+  const long n8 = (long)T * H / 8;         // H % 128 == 0
+  if (n8 == 0) return hipSuccess;
+  k_quant_rows_fp8<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(x, n8, codes,
                                                                scales);
   return hipGetLastError();
 }

@@ -23,6 +23,10 @@
  *    NULL means the null stream).  Calls return once work is enqueued.
  *  - Row-major layouts throughout.  bf16 data is passed as 16-bit patterns,
  *    fp8 data as one byte per element (OCP E4M3, "e4m3fn").
+ *  - Activation and output row arrays (x, x_perm, x_shared, y_perm,
+ *    y_shared, out) are 16-byte aligned, as any device allocator returns
+ *    them: the kernels move rows with 16-byte loads and stores.  A
+ *    misaligned one is INVALID_ARGUMENT.
  *  - Data-dependent sizes stay on the device: the number of local rows is
  *    offsets[P].  Row buffers are sized for the capacity
  *    cap = T * min(k, num_local) rows.

@@ -99,6 +99,20 @@ def test_missing_pointers_are_rejected():
                          check=False) == L.MOE_ERR_INVALID_ARGUMENT
 
 
+def test_misaligned_rows_are_rejected():
+    """Row arrays move with 16-byte accesses; a pointer off a 16-byte
+    boundary is refused on the host before anything is enqueued."""
+    p = good()
+    assert m.moe_combine(p, 256, 256, 256, None, 256 + 8, stream=0,
+                         check=False) == L.MOE_ERR_INVALID_ARGUMENT
+    assert m.moe_combine(p, 256 + 4, 256, 256, None, 256, stream=0,
+                         check=False) == L.MOE_ERR_INVALID_ARGUMENT
+    need = m.moe_dispatch_workspace_size(p)
+    st = m.moe_dispatch(p, 256 + 2, 256, 256, None, None, 256, None, 256, 256,
+                        256, 256, 256, need, stream=0, check=False)
+    assert st == L.MOE_ERR_INVALID_ARGUMENT
+
+
 def test_small_workspace_is_rejected():
     p = good()
     need = m.moe_dispatch_workspace_size(p)
