@@ -244,7 +244,11 @@ moe_status moe_check_problem(const moe_problem* p) {
   } else if (a == MOE_BF16 && w == MOE_BF16) {
     if (p->H % 128 || p->I % 128) return MOE_ERR_UNSUPPORTED;
   } else if (a == MOE_BF16 && w == MOE_FP8_E4M3) {
-    if (p->quant_block != 128 || p->H % 128 || p->I % 128) return MOE_ERR_UNSUPPORTED;
+    // reductions of at most 128 scale blocks (the kernels keep a tile's
+    // weight-scale column in LDS)
+    if (p->quant_block != 128 || p->H % 128 || p->I % 128 || p->H > 16384 ||
+        p->I > 16384)
+      return MOE_ERR_UNSUPPORTED;
   } else {
     return MOE_ERR_UNSUPPORTED;
   }
@@ -449,7 +453,7 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
     extras.tiles = L.f.tiles;
     extras.tile_count = L.f.tile_count;
     extras.BM = ffn_tile_rows(p->act_dtype, p->weight_dtype, rows_hint(p),
-                              p->H, &extras.balanced);
+                              p->H, p->I, &extras.balanced);
     extras.has_shared = p->has_shared;
   }
   // the router's count pass stores every entry of counts (no zero fill)

@@ -81,6 +81,31 @@ __device__ __forceinline__ int tile_split(int rows, int BM, int balanced,
   return (rows + p - 1) / p;
 }
 
+// ------------------------------------------------------ LDS ring helpers
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 left at maximum).
+#define WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (0xF << 8))
+
+// Workgroup barrier for the LDS ring.  The stage about to be read was written
+// by global_load_lds (tracked by vmcnt, waited for with WAIT_VMCNT by every
+// wavefront before it arrives here); the stage about to be overwritten was
+// read into registers that the MFMAs before this point consumed (lgkmcnt is
+// drained here).  A memory-model fence would also drain the prefetches still
+// in flight, so only the compiler is fenced.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0), vmcnt/expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 static inline size_t moe_align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 static inline int moe_ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
@@ -178,13 +203,14 @@ hipError_t launch_ffn(FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_fp8(FfnArgs& a, hipStream_t s);
 // rows per tile the FFN uses for this recipe and expected group size; sets
 // *balanced when a group's tiles are near-equal multiples of 16 rows
-int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int* balanced);
+int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int I, int* balanced);
+int ffn_fp8_tile_rows(int rows_hint, int H, int I, int* balanced);
 // gate/up LDS-ring GEMM over a list of tiles of up to gemm_tile_rows() rows
 hipError_t launch_gemm_bf16_gateup(const FfnArgs& f, hipStream_t s);
 int gemm_tile_rows();
 hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
-                              int T, int BM, int4* tiles, int32_t* count,
-                              hipStream_t s);
+                              int T, int BM, int balanced, int4* tiles,
+                              int32_t* count, hipStream_t s);
 
 // natural output-major [R][C] -> packed operand blocks (bf16: 16x32 blocks;
 // fp8: 16x128 blocks)

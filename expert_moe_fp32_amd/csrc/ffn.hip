@@ -433,20 +433,20 @@ hipError_t launch_pack_bf16(const bf16_t* src, int R, int C, void* dst,
 // for down (its own list of 128-row tiles).
 static bool bf16_streaming(int rows_hint) { return rows_hint <= 32; }
 
-int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int* balanced) {
-  (void)H;
+int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int I, int* balanced) {
   *balanced = 0;
-  if (act == MOE_F32 || wdt == MOE_FP8_E4M3) return TBM;
+  if (wdt == MOE_FP8_E4M3) return ffn_fp8_tile_rows(rows_hint, H, I, balanced);
+  if (act == MOE_F32) return TBM;
   if (bf16_streaming(rows_hint)) return 32;
   *balanced = 1;
   return gemm_tile_rows();
 }
 
 hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
-                              int T, int BM, int4* tiles, int32_t* count,
-                              hipStream_t s) {
-  k_build_tiles<<<1, 1024, 0, s>>>(offsets, P, has_shared, T, BM, 0, tiles,
-                                   count, BM, nullptr, nullptr);
+                              int T, int BM, int balanced, int4* tiles,
+                              int32_t* count, hipStream_t s) {
+  k_build_tiles<<<1, 1024, 0, s>>>(offsets, P, has_shared, T, BM, balanced,
+                                   tiles, count, BM, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -458,7 +458,7 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   // expert (decode) stream the weights; hundreds (prefill) tile through LDS.
   const bool f32 = f.act == MOE_F32;
   int balanced;
-  const int BM = ffn_tile_rows(f.act, f.wdt, f.rows_hint, f.H, &balanced);
+  const int BM = ffn_tile_rows(f.act, f.wdt, f.rows_hint, f.H, f.I, &balanced);
   const bool stream = !f32 && BM == 32;
   const bool ring = !f32 && balanced;     // tiles of up to 256 rows
   // the ring GEMM's list (or the only list), plus down's 128-row list; a

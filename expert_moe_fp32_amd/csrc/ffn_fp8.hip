@@ -49,6 +49,11 @@ struct K8Args {
 
 enum { M8_GATEUP = 0, M8_DOWN = 1 };
 
+// Weight-scale columns are copied to LDS per tile (a global load of one
+// inside a K loop would sit behind that loop's prefetches on the in-order
+// vector-memory counter); up to kMaxKB scale blocks, i.e. K <= 16384.
+static constexpr int kMaxKB = 128;
+
 __device__ __forceinline__ f32x4_t mfma_fp8(i32x8_t a, i32x8_t b) {
   const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -71,6 +76,7 @@ __global__ __launch_bounds__(256) void k_tile_fp8(K8Args a) {
   __shared__ u32x4_t lds_a[2][8 * 128];
   __shared__ u32x4_t lds_b[2][8 * 128];
   __shared__ float lds_s[2][128];
+  __shared__ float lds_w[2][kMaxKB];        // the tile's weight-scale columns
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
@@ -148,6 +154,10 @@ __global__ __launch_bounds__(256) void k_tile_fp8(K8Args a) {
       lds_b[0][tid + 256 * j] = rb[j];
     }
     if (tid < 128) lds_s[0][tid] = rs;
+    for (int i = tid; i < KB; i += 256) {     // (the barrier above freed it)
+      lds_w[0][i] = sw0[i];
+      if (MODE == M8_GATEUP) lds_w[1][i] = sw1[i];
+    }
     __syncthreads();
     for (int kt = 0; kt < KB; ++kt) {
       const int cur = kt & 1;
@@ -160,8 +170,8 @@ __global__ __launch_bounds__(256) void k_tile_fp8(K8Args a) {
         }
         if (srow) rs = srow[kt + 1];
       }
-      const float w0s = sw0[kt];
-      const float w1s = MODE == M8_GATEUP ? sw1[kt] : w0s;
+      const float w0s = lds_w[0][kt];
+      const float w1s = MODE == M8_GATEUP ? lds_w[1][kt] : w0s;
       i32x8_t fb[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -227,32 +237,227 @@ __global__ __launch_bounds__(256) void k_tile_fp8(K8Args a) {
   }
 }
 
+// ------------------------------------------------------ LDS-ring kernel
+// For groups of up to 16 * NMB rows (one tile per expert at prefill-like
+// batches of ~130 rows per expert, a few rows at decode).  A workgroup of 8
+// wavefronts owns one tile and a group of output channels; each wavefront
+// owns two 16-channel weight columns -- gate and up of the same channels
+// (128 channels an item), or two down columns 128 channels apart (256 an
+// item) -- so each weight byte is read once per tile, the tile's activation
+// rows are re-read once per 128 (256) channels, and the SiLU epilogue needs
+// no exchange.  Operands come through a ring of 3 LDS stages of one 128-wide
+// K block each (one scale block) that global_load_lds fills two stages ahead
+// without holding registers.  A stage holds the tile's activation blocks
+// (NMB of 2 KiB, lane order), the 16 weight blocks (2 KiB each) and the tile
+// rows' scales.  Every wavefront issues the same number of loads per stage
+// (A_PER activation half-blocks -- ids past 2 * NMB repeat the last one,
+// writing identical bytes -- four weight halves and one 64-row scale slice;
+// wavefronts past the last slice load 256 contiguous bytes into a dump
+// slot), so "this stage has landed" is one fixed vmcnt.  The weight scales
+// of the two columns sit one per lane (K <= 16384) and are read with
+// readlane, so the loop issues no global load of its own.
+template <int MODE, int NMB>
+__global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
+  constexpr int NAB = 2 * NMB;                   // activation half-blocks
+  constexpr int A_PER = (NAB + 7) / 8;
+  constexpr int NRS = (16 * NMB + 63) / 64;      // 64-row scale slices
+  constexpr int C = A_PER + 4 + 1;               // loads per stage per wave
+  __shared__ u32x4_t la0[NMB * 128], la1[NMB * 128], la2[NMB * 128];
+  __shared__ u32x4_t lb0[16 * 128], lb1[16 * 128], lb2[16 * 128];
+  __shared__ __attribute__((aligned(16))) float ls0[(NRS + 1) * 64],
+      ls1[(NRS + 1) * 64], ls2[(NRS + 1) * 64];  // slice NRS: dump slot
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, q = lane >> 4;
+  const int K = a.K, KB = K / 128;
+  const int total = a.tile_count[0] * a.nb_per_tile;
+  const int G = gridDim.x, per_xcd = G >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  for (int base = 0; base < total; base += G) {
+    const int item = base + xcd * per_xcd + slot;
+    if (item >= total) continue;                 // uniform for the workgroup
+    const int tile = item / a.nb_per_tile;
+    const int nb = item - tile * a.nb_per_tile;
+    const int4 td = a.tiles[tile];
+    const int g = td.x, row0 = td.y, nrows = td.z;
+    const bool sh = g == a.P;
+    const int nmb = (nrows + 15) >> 4;
+    const uint8_t* abase = sh ? a.a_shared : a.a_routed;
+    const float* sbase = sh ? a.as_shared : a.as_routed;
+    auto src_row = [&](int r) -> int {           // tile row -> source row
+      if (r >= nrows) r = 0;                     // padded rows read row 0
+      const int rr = row0 + r;
+      return sh ? rr : (a.a_rows ? a.a_rows[rr] : rr);
+    };
+    // activation half-blocks of this wavefront: id = wv + 8 i (clamped)
+    int arow[A_PER], aid[A_PER];
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      aid[i] = min(wv + 8 * i, NAB - 1);
+      arow[i] = src_row((aid[i] >> 1) * 16 + (lane & 15));
+    }
+    const int aoff = 32 * (lane >> 4);
+    // scale slice (rows 64 wv + lane) or the dump slot
+    const bool sreal = wv < NRS;
+    const int srow = src_row(64 * (sreal ? wv : 0) + lane);
+    // the two weight columns of this wavefront
+    int cb0, cb1;
+    const void *W0, *W1;
+    const float *S0, *S1;
+    if (MODE == M8_GATEUP) {
+      cb0 = cb1 = nb * 8 + wv;
+      W0 = sh ? a.w0_sh : a.w0_arr[g];
+      W1 = sh ? a.w1_sh : a.w1_arr[g];
+      S0 = sh ? a.s0_sh : a.s0_arr[g];
+      S1 = sh ? a.s1_sh : a.s1_arr[g];
+    } else {
+      cb0 = nb * 16 + wv;
+      cb1 = cb0 + 8;
+      W0 = W1 = sh ? a.w0_sh : a.w0_arr[g];
+      S0 = S1 = sh ? a.s0_sh : a.s0_arr[g];
+    }
+    const u32x4_t* wp0 = (const u32x4_t*)W0 + (size_t)cb0 * KB * 128 + lane;
+    const u32x4_t* wp1 = (const u32x4_t*)W1 + (size_t)cb1 * KB * 128 + lane;
+    // dump-slot source: 256 contiguous bytes of the column's own block
+    const float* sdump = (const float*)((const u32x4_t*)W0 + (size_t)cb0 * KB * 128) + lane;
+    // weight scales, one K block per lane (two registers cover KB <= 128)
+    const float* sc0 = S0 + (size_t)(cb0 >> 3) * KB;
+    const float* sc1 = S1 + (size_t)(cb1 >> 3) * KB;
+    const float w0lo = lane < KB ? sc0[lane] : 0.f;
+    const float w0hi = lane + 64 < KB ? sc0[lane + 64] : 0.f;
+    const float w1lo = lane < KB ? sc1[lane] : 0.f;
+    const float w1hi = lane + 64 < KB ? sc1[lane + 64] : 0.f;
+    auto wscale = [&](float lo, float hi, int kb) -> float {
+      const float v = kb < 64 ? lo : hi;
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kb & 63));
+    };
+
+    auto issue = [&](int kb, u32x4_t* A, u32x4_t* B, float* S) {
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) {
+        const int id = aid[i];
+        lds_dma16(abase + (size_t)arow[i] * K + kb * 128 + aoff + 16 * (id & 1),
+                  A + (id >> 1) * 128 + (id & 1) * 64);
+      }
+      lds_dma16(wp0 + (size_t)kb * 128, B + wv * 128);
+      lds_dma16(wp0 + (size_t)kb * 128 + 64, B + wv * 128 + 64);
+      lds_dma16(wp1 + (size_t)kb * 128, B + (8 + wv) * 128);
+      lds_dma16(wp1 + (size_t)kb * 128 + 64, B + (8 + wv) * 128 + 64);
+      const float* sg = sreal ? sbase + (size_t)srow * KB + kb
+                              : sdump + (size_t)kb * 512;
+      __builtin_amdgcn_global_load_lds(sg, (lds_void*)(S + 64 * (sreal ? wv : NRS)),
+                                       4, 0, 0);
+    };
+    f32x4_t acc0[NMB], acc1[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      acc0[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc1[mb] = acc0[mb];
+    }
+    // All NMB row blocks run, straight-line, whatever nrows is: the MFMAs
+    // are cheap next to the weight stream, and a branch per block would
+    // make every block wait out its own LDS latency.  Padded rows hold row
+    // 0's data and are never stored.
+    auto compute = [&](int kb, const u32x4_t* A, const u32x4_t* B, const float* S) {
+      const float ws0 = wscale(w0lo, w0hi, kb);
+      const float ws1 = wscale(w1lo, w1hi, kb);
+      const i32x8_t fb0 = join(B[wv * 128 + lane], B[wv * 128 + 64 + lane]);
+      const i32x8_t fb1 = join(B[(8 + wv) * 128 + lane], B[(8 + wv) * 128 + 64 + lane]);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const i32x8_t fa = join(A[mb * 128 + lane], A[mb * 128 + 64 + lane]);
+        const f32x4_t sa = *(const f32x4_t*)(S + mb * 16 + 4 * q);
+        const f32x4_t p0 = mfma_fp8(fa, fb0);
+        const f32x4_t p1 = mfma_fp8(fa, fb1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc0[mb][r] = __builtin_fmaf(p0[r], sa[r] * ws0, acc0[mb][r]);
+          acc1[mb][r] = __builtin_fmaf(p1[r], sa[r] * ws1, acc1[mb][r]);
+        }
+        if ((mb & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound hoisting
+      }
+    };
+    lds_barrier();                               // last item done with the ring
+    issue(0, la0, lb0, ls0);
+    issue(min(1, KB - 1), la1, lb1, ls1);
+    // Three stages per trip; past the end a step re-issues the last K block
+    // into a slot that is never read and computes nothing, so exactly one
+    // later stage (C loads) is in flight at every wait.
+    for (int kb = 0; kb < KB; kb += 3) {
+#define RING_STEP(J, AC, BC, SC, AN, BN, SN)                    \
+      {                                                         \
+        const int k = kb + J;                                   \
+        WAIT_VMCNT(C);                                          \
+        lds_barrier();                                          \
+        issue(k + 2 < KB ? k + 2 : KB - 1, AN, BN, SN);         \
+        if (k < KB) compute(k, AC, BC, SC);                     \
+        __builtin_amdgcn_sched_barrier(0);                      \
+      }
+      RING_STEP(0, la0, lb0, ls0, la2, lb2, ls2)
+      RING_STEP(1, la1, lb1, ls1, la0, lb0, ls0)
+      RING_STEP(2, la2, lb2, ls2, la1, lb1, ls1)
+#undef RING_STEP
+    }
+    WAIT_VMCNT(0);                               // trailing re-reads landed
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      if (mb >= nmb) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = mb * 16 + 4 * q + r;
+        if (lr >= nrows) continue;
+        if (MODE == M8_GATEUP) {
+          const size_t hr = (size_t)(sh ? a.cap : 0) + row0 + lr;
+          a.h_out[hr * a.N + cb0 * 16 + c16] = silu_f32(acc0[mb][r]) * acc1[mb][r];
+        } else {
+          float* y = (sh ? a.y_shared : a.y_routed) + (size_t)(row0 + lr) * a.N;
+          y[cb0 * 16 + c16] = acc0[mb][r];
+          y[cb1 * 16 + c16] = acc1[mb][r];
+        }
+      }
+    }
+  }
+}
+
 // Quantise float32 h rows per 128 channels: routed rows [0, N) (N read on the
-// device) and shared rows [cap, cap + T_sh).  One wavefront per group.
+// device) and shared rows [cap, cap + T_sh).  A lane takes 8 channels (two
+// 16-byte loads), the 16 lanes of a DPP row one 128-channel group.
+__device__ __forceinline__ float row16_max(float v) {
+#define ROWF(ctrl)                                                            \
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(                    \
+                   0, __float_as_int(v), ctrl, 0xF, 0xF, false)));
+  ROWF(0x128) ROWF(0x124) ROWF(0x122) ROWF(0x121)
+#undef ROWF
+  return v;
+}
+
 __global__ __launch_bounds__(256) void k_quant_h_fp8(
     const float* __restrict__ h, int I, const int32_t* __restrict__ n_routed,
     int cap, int T_sh, uint8_t* __restrict__ codes,
     float* __restrict__ scales) {
-  const int GI = I / 128;
-  const long rows = (long)(*n_routed) + T_sh;
-  const long groups = rows * GI;
-  const int lane = threadIdx.x & 63;
-  for (long grp = (long)blockIdx.x * 4 + (threadIdx.x >> 6); grp < groups;
-       grp += (long)gridDim.x * 4) {
-    const long ri = grp / GI;
-    const int gi = (int)(grp - ri * GI);
-    const long hr = ri < *n_routed ? ri : cap + (ri - *n_routed);
-    const float* src = h + hr * I + gi * 128;
-    const float v0 = src[2 * lane], v1 = src[2 * lane + 1];
-    float amax = fmaxf(fabsf(v0), fabsf(v1));
+  const int CI = I / 8;                          // chunks of 8 per row
+  const long nr = *n_routed;
+  const long total = (nr + T_sh) * CI;           // a multiple of 16
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (long)gridDim.x * 256) {
+    const long ri = i / CI;
+    const int ci = (int)(i - ri * CI);
+    const long hr = ri < nr ? ri : cap + (ri - nr);
+    const f32x4_t* src = (const f32x4_t*)(h + hr * I + 8 * ci);
+    const f32x4_t v0 = src[0], v1 = src[1];
+    float amax = 0.0f;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fmaxf(fabsf(v0[r]), fabsf(v1[r])));
+    amax = row16_max(amax);
     const float sc = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
-    const uint8_t c0 = f32_to_e4m3(__fdiv_rn(v0, sc));
-    const uint8_t c1 = f32_to_e4m3(__fdiv_rn(v1, sc));
-    *(uint16_t*)(codes + hr * I + gi * 128 + 2 * lane) =
-        (uint16_t)c0 | ((uint16_t)c1 << 8);
-    if (lane == 0) scales[hr * GI + gi] = sc;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      lo |= (uint32_t)f32_to_e4m3(__fdiv_rn(v0[r], sc)) << (8 * r);
+      hi |= (uint32_t)f32_to_e4m3(__fdiv_rn(v1[r], sc)) << (8 * r);
+    }
+    *(uint2*)(codes + hr * I + 8 * ci) = make_uint2(lo, hi);
+    if ((threadIdx.x & 15) == 0) scales[hr * (I / 128) + ci / 16] = sc;
   }
 }
 
@@ -284,13 +489,37 @@ hipError_t launch_pack_fp8(const uint8_t* src, int R, int C, void* dst,
   return hipGetLastError();
 }
 
+// Tile rows of the FP8 recipe for an expected group size: the LDS-ring
+// weight-streaming kernel with 32-row tiles (a few rows per expert) or
+// 160-row tiles (one tile per expert up to 160 rows), both balanced; else
+// the 128 x 128 tiled kernel.  The ring's down pass covers 256 channels an
+// item, so it needs H % 256 == 0.
+int ffn_fp8_tile_rows(int rows_hint, int H, int I, int* balanced) {
+  (void)I;
+  *balanced = 0;
+  if (H % 256 || rows_hint > 160) return 128;
+  *balanced = 1;
+  return rows_hint <= 24 ? 32 : 160;
+}
+
+template <int MODE>
+static void launch_stream_fp8(const K8Args& a, int BM, hipStream_t s) {
+  // one workgroup per CU (LDS); a multiple of 8 for the XCD-major order
+  if (BM == 32)
+    k_ring_fp8<MODE, 2><<<256, 512, 0, s>>>(a);
+  else
+    k_ring_fp8<MODE, 10><<<256, 512, 0, s>>>(a);
+}
+
 hipError_t launch_ffn_fp8(FfnArgs& f, hipStream_t s) {
   const int G = f.P + (f.has_shared ? 1 : 0);
   if (G == 0) return hipSuccess;
-  const int BM = 128;
+  int balanced;
+  const int BM = ffn_fp8_tile_rows(f.rows_hint, f.H, f.I, &balanced);
+  const bool stream = balanced != 0;
   if (!f.tiles_ready)
-    launch_build_tiles(f.offsets, f.P, f.has_shared, f.T, BM, f.tiles,
-                       f.tile_count, s);
+    launch_build_tiles(f.offsets, f.P, f.has_shared, f.T, BM, balanced,
+                       f.tiles, f.tile_count, s);
   if (f.events) hipEventRecord(f.events[0], s);
   const long hrows = (long)f.cap + (f.has_shared ? f.T : 0);
   const long max_tiles = G + hrows / BM + 1;
@@ -318,16 +547,18 @@ hipError_t launch_ffn_fp8(FfnArgs& f, hipStream_t s) {
   a.s0_sh = w->sh_s_gate;
   a.s1_sh = w->sh_s_up;
   a.h_out = f.h32;
-  a.nb_per_tile = a.N / 64;
+  a.nb_per_tile = a.N / (stream ? 128 : 64);
   long items = max_tiles * a.nb_per_tile;
   long grid = items < cu * 2 ? items : cu * 2;
-  k_tile_fp8<M8_GATEUP><<<(unsigned)grid, 256, 0, s>>>(a);
+  if (stream)
+    launch_stream_fp8<M8_GATEUP>(a, BM, s);
+  else
+    k_tile_fp8<M8_GATEUP><<<(unsigned)grid, 256, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // ---- h -> E4M3 per row per 128 channels
   {
-    long groups = hrows * (f.I / 128);
-    long qg = (groups + 3) / 4;
+    long qg = (hrows * (f.I / 8) + 255) / 256;
     if (qg > 8192) qg = 8192;
     if (qg < 1) qg = 1;
     k_quant_h_fp8<<<(unsigned)qg, 256, 0, s>>>(
@@ -355,10 +586,13 @@ hipError_t launch_ffn_fp8(FfnArgs& f, hipStream_t s) {
   a.s1_sh = nullptr;
   a.y_routed = f.y_routed;
   a.y_shared = f.y_shared;
-  a.nb_per_tile = a.N / 128;
+  a.nb_per_tile = a.N / (stream ? 256 : 128);
   items = max_tiles * a.nb_per_tile;
   grid = items < cu * 2 ? items : cu * 2;
-  k_tile_fp8<M8_DOWN><<<(unsigned)grid, 256, 0, s>>>(a);
+  if (stream)
+    launch_stream_fp8<M8_DOWN>(a, BM, s);
+  else
+    k_tile_fp8<M8_DOWN><<<(unsigned)grid, 256, 0, s>>>(a);
   if (f.events) hipEventRecord(f.events[2], s);
   return hipGetLastError();
 }

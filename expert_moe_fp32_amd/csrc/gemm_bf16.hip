@@ -37,30 +37,6 @@ struct GArgs {
   bf16_t* h_out;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
-}
-
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 left at maximum).
-#define WAIT_VMCNT(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (0xF << 8))
-
-// Workgroup barrier for the LDS ring.  The stage about to be read was written
-// by global_load_lds (tracked by vmcnt, waited for with WAIT_VMCNT by every
-// wavefront before it arrives here); the stage about to be overwritten was
-// read into registers that the MFMAs before this point consumed (lgkmcnt is
-// drained here).  A memory-model fence would also drain the prefetches still
-// in flight, so only the compiler is fenced.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0), vmcnt/expcnt untouched
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 __device__ __forceinline__ f32x4_t mfma16b(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b),

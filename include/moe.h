@@ -70,7 +70,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
  *   act BF16, weight BF16,     out BF16|F32 (bf16 MFMA, fp32 accumulate)
  *   act BF16, weight FP8_E4M3, out BF16|F32 (activations quantised to E4M3
  *        per token per quant_block channels; fp8 MFMA, fp32 accumulate)
- * The FP8 recipe needs H and I to be multiples of quant_block (= 128). */
+ * The FP8 recipe needs H and I to be multiples of quant_block (= 128) and at
+ * most 16384. */
 typedef struct {
   int32_t T;            /* tokens on this rank                               */
   int32_t H;            /* hidden size                                       */

@@ -60,6 +60,7 @@ def good(**kw):
     (dict(act="f32", wdt="f32", out="f32", H=36, I=20), L.MOE_OK),
     (dict(wdt="fp8", quant_block=64), L.MOE_ERR_UNSUPPORTED),
     (dict(wdt="fp8"), L.MOE_OK),
+    (dict(wdt="fp8", H=16384 + 128), L.MOE_ERR_UNSUPPORTED),
     (dict(E=2000, k=2, num_local=8), L.MOE_ERR_UNSUPPORTED),
 ])
 def test_problem_validation(kw, status):

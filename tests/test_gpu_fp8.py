@@ -73,9 +73,23 @@ def run_fp8_layer(wl):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(T=200, H=256, I=256, E=16, num_local=8, k=4),            # ragged tiles
-    dict(T=40, H=384, I=128, E=64, num_local=16, k=4),            # few rows
-    dict(T=300, H=256, I=128, E=8, num_local=8, k=2, shared=True),  # shared
+    # LDS-ring weight streaming, 160-row tiles (one per expert), ragged;
+    # gate/up runs two trips of its 4-stage loop
+    dict(T=200, H=1024, I=512, E=16, num_local=8, k=4),
+    # LDS-ring weight streaming, 32-row tiles (a few rows per expert)
+    dict(T=64, H=512, I=512, E=32, num_local=8, k=4),
+    # LDS-ring streaming with the shared expert's 300 rows in 160-row tiles
+    dict(T=300, H=512, I=512, E=8, num_local=8, k=2, shared=True),
+    # 128 x 128 tiled kernel (H not a multiple of 256; many rows per
+    # expert), and the ring with a one-K-block down pass (I = 128).
+    # (When fp32 and float64 accumulation put an h element on opposite sides
+    # of an E4M3 rounding boundary, that one code moves an output by about
+    # |dh| |w_down|, i.e. ~1/sqrt(I) of the output RMS scaled by how large
+    # that h and w are; with 1400 rows at I = 256 the largest such case
+    # reaches the 4e-2 bar by itself, so the many-rows case uses I = 512.)
+    dict(T=40, H=384, I=128, E=64, num_local=16, k=4),
+    dict(T=300, H=256, I=128, E=8, num_local=8, k=2, shared=True),
+    dict(T=700, H=256, I=512, E=8, num_local=8, k=2),
 ])
 def test_fp8_layer_reduced(kw):
     wl = make_workload("fp8", seed=31, **kw)
