@@ -41,6 +41,48 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 
 
+# HBM bytes per launch of each workload's dominant (gate/up) kernel from two
+# rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# each scaled by the factor that makes the same counter read the known size
+# of the weight-prepack kernel in the same run (profiles/ has the commands
+# and the tables).  The figures hold for the kernel source they were taken
+# on: when the SHA-256 of its files differs, traffic is reported as null.
+TRAFFIC = {
+    "decode": dict(kernel="k_stream_bf16<0, 2>",
+                   files=("expert_moe_fp32_amd/csrc/ffn.hip",
+                          "expert_moe_fp32_amd/csrc/common.h"),
+                   sha="9fc2192c5d0f462a", fetch_kib=794481.0, write_kib=988.3,
+                   fetch_factor=1.9977, write_factor=1.0),
+    "prefill": dict(kernel="k_gemm_bf16<4, 4>",
+                    files=("expert_moe_fp32_amd/csrc/gemm_bf16.hip",
+                           "expert_moe_fp32_amd/csrc/common.h"),
+                    sha="9fd786ff6a12c7ae", fetch_kib=2166375.0,
+                    write_kib=106888.0, fetch_factor=1.998, write_factor=1.0),
+    "fp8": dict(kernel="k_ring_fp8<0, 10>",
+                files=("expert_moe_fp32_amd/csrc/ffn_fp8.hip",
+                       "expert_moe_fp32_amd/csrc/common.h"),
+                sha="ab485ca6ee1357c3", fetch_kib=474027.7, write_kib=33232.0,
+                fetch_factor=1.9956, write_factor=1.0),
+}
+
+
+def traffic_bytes(workload):
+    """Counter-derived HBM bytes per launch, or None (no counters for this
+    workload, or the kernel's source changed since they were taken)."""
+    import hashlib
+    t = TRAFFIC.get(workload)
+    if t is None:
+        return None
+    h = hashlib.sha256()
+    for f in t["files"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != t["sha"]:
+        return None
+    return int((t["fetch_kib"] * t["fetch_factor"] +
+                t["write_kib"] * t["write_factor"]) * 1024)
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -248,11 +290,12 @@ def main():
     prec = "fp8" if wl.wdt == "fp8" else wl.act
     ridge = MFMA_PEAK_TFLOPS[prec] * 1e12 / (HBM_PEAK_GBPS * 1e9)
     ai = u["gu_flops"] / u["gu_bytes"]
+    traffic = traffic_bytes(args.workload)
     if ai < ridge:
         achieved = u["gu_bytes"] / gu_s / 1e9
         roof = dict(bound="hbm", kernel="gate_up", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic,
                     algorithmic_bytes=int(u["gu_bytes"]),
                     avg_us=round(gu_s * 1e6, 2))
     else:
@@ -260,7 +303,7 @@ def main():
         roof = dict(bound="mfma", kernel="gate_up", achieved=round(achieved, 1),
                     peak=MFMA_PEAK_TFLOPS[prec], unit="TFLOP/s",
                     frac=round(achieved / MFMA_PEAK_TFLOPS[prec], 4),
-                    traffic=None, algorithmic_flops=u["gu_flops"],
+                    traffic=traffic, algorithmic_flops=u["gu_flops"],
                     avg_us=round(gu_s * 1e6, 2))
 
     # whole-layer roofline: the larger of the flop time at the MFMA peak and

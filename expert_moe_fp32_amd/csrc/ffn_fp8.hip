@@ -289,11 +289,16 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
       const int rr = row0 + r;
       return sh ? rr : (a.a_rows ? a.a_rows[rr] : rr);
     };
-    // activation half-blocks of this wavefront: id = wv + 8 i (clamped)
+    // activation half-blocks of this wavefront (id = 2 mb + half): with two
+    // or more per wavefront, both halves of row block wv come first, back to
+    // back, so the second finds the rows' cache lines in L1; the rest are
+    // dealt round-robin (ids past the last repeat it)
     int arow[A_PER], aid[A_PER];
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-      aid[i] = min(wv + 8 * i, NAB - 1);
+      const int id = A_PER >= 2 ? (i < 2 ? 2 * wv + i : 16 + 8 * (i - 2) + wv)
+                                : wv;
+      aid[i] = min(id, NAB - 1);
       arow[i] = src_row((aid[i] >> 1) * 16 + (lane & 15));
     }
     const int aoff = 32 * (lane >> 4);
