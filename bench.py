@@ -11,7 +11,11 @@ Workloads: tiny, decode, prefill, skewed (prefill shape with a Zipf logit
 bias, identity placement), skewed_eplb (the same batch with the 8 hottest
 local experts given a second physical copy, placed from the first pass's
 expert counts by the library's moe_eplb_hottest_map; the layer then reads 40
-physical experts' weights), fp8.
+physical experts' weights), fp8, lowlat (128-token FP8 decode batch).
+
+--graph captures one layer forward into a HIP graph (torch.cuda.CUDAGraph on
+the library's stream argument) and times graph replays; the line then also
+carries the eager per-step time.
 
 Besides throughput the line carries:
 * roofline: the dominant kernel's algorithmic bytes (or flops) per launch over
@@ -177,7 +181,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["tiny", "decode", "prefill", "skewed",
-                             "skewed_eplb", "fp8"])
+                             "skewed_eplb", "fp8", "lowlat"])
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph of one step")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the CPU oracle baseline leg")
@@ -243,9 +249,39 @@ def main():
     def step():
         dl.forward(b, dlog, dbias, dx)
 
+    def timed(fn, k):
+        e0, e1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(e0, torch.cuda.current_stream().cuda_stream)
+        for _ in range(k):
+            fn()
+        hip.record(e1, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        ms = hip.ms(e0, e1) / k
+        hip.destroy(e0)
+        hip.destroy(e1)
+        return ms
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    eager_ms = None
+    if args.graph:
+        eager_ms = timed(step, args.steps)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        step = graph.replay
     # ---- timed region: exactly K layer forwards
     e0, e1 = hip.event(), hip.event()
     torch.cuda.synchronize()
@@ -347,6 +383,9 @@ def main():
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "down_GBps": round(u["dn_bytes"] / dn_s / 1e9, 1),
     }
+    if args.graph:
+        result["graph"] = {"replay_us_per_step": round(ms_per_step * 1e3, 2),
+                           "eager_us_per_step": round(eager_ms * 1e3, 2)}
     if wl.name == "skewed":
         lc = local_counts.astype(np.float64)
         pc = phys_counts.astype(np.float64)
@@ -359,7 +398,7 @@ def main():
         }
     if not args.no_cpu:
         n = args.cpu_tokens or {"tiny": 128, "decode": 256, "prefill": 16,
-                                "skewed": 16, "fp8": 16}[wl.name]
+                                "skewed": 16, "fp8": 16, "lowlat": 8}[wl.name]
         rng = np.random.default_rng(1)
         tok = np.sort(rng.choice(wl.T, size=min(n, wl.T), replace=False))
         log(f"bench: CPU oracle on {len(tok)} tokens ...")

@@ -17,6 +17,11 @@ always-on shared expert, one EP rank's contiguous share of experts):
   skew as the power-law load simulation of the infra-guide page, section 5.2).
 * ``fp8``     DeepSeek-V3 shape, T=4096, no shared expert; fp32 master weights
   that each side quantises to OCP E4M3 with one fp32 scale per 128x128 block.
+* ``lowlat``  the low-latency decode setting of DeepEP's low-latency kernels as
+  the infra-guide page, section 6.1, gives it: 128 tokens a batch, hidden 7168,
+  top-8, FP8 dispatch (activations in E4M3 per token per 128 channels) and
+  BF16 combine; the expert is DeepSeek-V3's (I=2048, 256 experts, 32 local),
+  weights as in ``fp8``.
 
 Stored layouts (row-major):
 * ``logits`` [T, E] float32, ``bias`` [E] float32 or None;
@@ -55,6 +60,9 @@ CONFIGS: Dict[str, dict] = {
     "fp8": dict(wid=5, T=4096, H=7168, I=2048, E=256, k=8, expert_begin=0,
                 num_local=32, shared=False, act="bf16", wdt="fp8", out="bf16",
                 bias=None, quant_block=128),
+    "lowlat": dict(wid=6, T=128, H=7168, I=2048, E=256, k=8, expert_begin=0,
+                   num_local=32, shared=False, act="bf16", wdt="fp8",
+                   out="bf16", bias=None, quant_block=128),
 }
 
 _TENSOR_LOGITS, _TENSOR_X, _TENSOR_W, _TENSOR_SHARED, _TENSOR_PERM = 1, 2, 3, 4, 5
