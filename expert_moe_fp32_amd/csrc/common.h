@@ -207,6 +207,7 @@ int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int I, int* balanced);
 int ffn_fp8_tile_rows(int rows_hint, int H, int I, int* balanced);
 // gate/up LDS-ring GEMM over a list of tiles of up to gemm_tile_rows() rows
 hipError_t launch_gemm_bf16_gateup(const FfnArgs& f, hipStream_t s);
+hipError_t launch_gemm_bf16_down(const FfnArgs& f, hipStream_t s);
 int gemm_tile_rows();
 hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
                               int T, int BM, int balanced, int4* tiles,

@@ -18,15 +18,17 @@
 // 16-B load per lane reads 1 KiB of contiguous memory, and 16 output
 // channels over the whole reduction are one contiguous run.
 //
-// Two bf16 kernels share the tile list:
+// bf16 kernels on the tile list:
 //  * k_stream_bf16 (groups of a few rows, decode): each wavefront streams its
 //    16 output channels' contiguous run straight into MFMA operand registers
 //    with non-temporal loads, one 128-wide K chunk ahead; every weight byte
 //    is read once per tile.
-//  * k_tile_bf16 (groups of hundreds of rows, prefill): 128 rows x 128
-//    columns per workgroup, double-buffered LDS holding operand blocks in
-//    lane order (conflict-free 16-B reads, no padding), 2x2 wavefronts of
-//    64 x 64.
+//  * k_gemm_bf16 (gemm_bf16.hip; groups of hundreds of rows, prefill): the
+//    256 x 256 LDS-ring GEMM for gate/up and down.
+//  * k_tile_bf16: 128 rows x 128 columns per workgroup, double-buffered LDS
+//    holding operand blocks in lane order (conflict-free 16-B reads, no
+//    padding), 2x2 wavefronts of 64 x 64; the down pass when H is not a
+//    multiple of 256.
 // The gate/up pass ends in the fused epilogue h = silu(g) * u rounded to
 // bf16; the down pass writes y in float32.
 //
@@ -428,9 +430,9 @@ hipError_t launch_pack_bf16(const bf16_t* src, int R, int C, void* dst,
 
 // -------------------------------------------------------------- driver
 // Kernel choice for the bf16 recipe: the weight-streaming kernel for a few
-// rows per group; for hundreds (prefill) the 256 x 256 LDS-ring GEMM for
-// gate/up (balanced tiles of up to 256 rows) and the 128 x 128 tiled kernel
-// for down (its own list of 128-row tiles).
+// rows per group; for hundreds (prefill) the 256 x 256 LDS-ring GEMM on
+// balanced tiles of up to 256 rows for gate/up and, when H % 256 == 0, for
+// down (else the 128 x 128 tiled kernel on its own list of 128-row tiles).
 static bool bf16_streaming(int rows_hint) { return rows_hint <= 32; }
 
 int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int I, int* balanced) {
@@ -505,14 +507,9 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
     long items = max_tiles * a.nb_per_tile;
     long grid = items < cu * 16 ? items : cu * 16;
     k_stream_bf16<MODE_GATEUP, 2><<<(unsigned)grid, 256, 0, s>>>(a);
-  } else if (ring) {
+  } else {                                  // ring: bf16 beyond streaming
     hipError_t e = launch_gemm_bf16_gateup(f, s);
     if (e != hipSuccess) return e;
-  } else {
-    a.nb_per_tile = a.N / 64;
-    long items = max_tiles * a.nb_per_tile;
-    long grid = items < cu * 2 ? items : cu * 2;
-    k_tile_bf16<MODE_GATEUP><<<(unsigned)grid, 256, 0, s>>>(a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -540,6 +537,9 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
     long items = max_tiles * a.nb_per_tile;
     long grid = items < cu * 16 ? items : cu * 16;
     k_stream_bf16<MODE_DOWN, 2><<<(unsigned)grid, 256, 0, s>>>(a);
+  } else if (ring && f.H % 256 == 0) {
+    hipError_t e = launch_gemm_bf16_down(f, s);
+    if (e != hipSuccess) return e;
   } else {
     if (ring) {
       a.tiles = f.tiles_down;

@@ -1,10 +1,11 @@
-// Prefill-shaped grouped bf16 GEMM for the gate/up half of the expert FFN,
-// with the fused SiLU epilogue, on the packed operand layout of ffn.hip.
+// Prefill-shaped grouped bf16 GEMM for the expert FFN -- gate/up with the
+// fused SiLU epilogue, and down -- on the packed operand layout of ffn.hip.
 //
-// Work item = (tile of <= 256 rows of one group, 128 gate + 128 up columns).
-// A workgroup of 4 wavefronts (2 x 2) computes 256 x 256 B-columns:
-// wavefront (wm, wn) owns 128 rows x 128 columns = 4 x 4 MFMA blocks of
-// 32 x 32 (256 fp32 accumulators per lane, one wavefront per SIMD).  The
+// Work item = (tile of <= 256 rows of one group, 128 gate + 128 up columns,
+// or 256 down columns).
+// A workgroup of 8 wavefronts (2 x 4) computes 256 x 256 B-columns:
+// wavefront (wm, wn) owns 128 rows x 64 columns = 4 x 2 MFMA blocks of
+// 32 x 32 (128 fp32 accumulators per lane, two wavefronts per SIMD).  The
 // reduction runs in 32-wide stages held in a ring of 4 LDS stages; each stage
 // is 16 A blocks + 16 B blocks of 1 KiB in lane order, filled by
 // global_load_lds_dwordx4 (each lane's 16 bytes land at block base + 16 *
@@ -34,8 +35,12 @@ struct GArgs {
   const void* const* w1_arr;
   const void* w0_sh;
   const void* w1_sh;
-  bf16_t* h_out;
+  bf16_t* h_out;              // gate/up output [cap + T][N]
+  float* y_routed;            // down output [cap][N]
+  float* y_shared;            // down output [T][N]
 };
+
+enum { G_GATEUP = 0, G_DOWN = 1 };
 
 __device__ __forceinline__ f32x4_t mfma16b(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -49,25 +54,26 @@ __device__ __forceinline__ f32x16_t mfma32b(u32x4_t a, u32x4_t b, f32x16_t c) {
                                                  c, 0, 0, 0);
 }
 
-// Workgroup = 2 x 2 wavefronts; wavefront (wm, wn) owns TM x TN blocks of
+// Workgroup = WM x WN wavefronts; wavefront (wm, wn) owns TM x TN blocks of
 // 32 x 32 computed with v_mfma_f32_32x32x16_bf16 (on gfx950 this instruction
-// sustains about 1.6x the rate of the 16x16x32 form), so a tile is 64*TM rows
-// x 64*TN B-columns.  Ring of 4 LDS stages of 32-wide K, each holding the
+// sustains about 1.6x the rate of the 16x16x32 form), so a tile is
+// 32*TM*WM rows x 32*TN*WN B-columns.  Ring of 4 LDS stages of 32-wide K, each holding the
 // tile's 16 x 32 operand blocks (1 KiB, lane order) as staged by
 // global_load_lds.  A 32 x 16 MFMA operand is read from two vertically
 // adjacent blocks: lane l takes row l % 32 (block (l % 32) / 16, its row
 // l % 16) and K-slot 2s + l / 32 of the stage's 32-wide K (substep s = 0, 1):
 // 16 lanes read 256 contiguous bytes, conflict-free.  The accumulator of lane
 // l holds column l % 32 and rows 8 * (r / 4) + 4 * (l / 32) + r % 4, r < 16.
-template <int TM, int TN>
-__global__ __launch_bounds__(256) void k_gemm_bf16(GArgs a) {
-  constexpr int NA = 4 * TM, NB = 4 * TN;          // 16-wide blocks per stage
-  constexpr int HA = NA / 4, HB = NB / 4;          // DMA per wavefront
+template <int MODE, int TM, int TN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
+  constexpr int NW = WM * WN;                      // wavefronts
+  constexpr int NA = 2 * TM * WM, NB = 2 * TN * WN;  // 16-wide blocks per stage
+  constexpr int HA = NA / NW, HB = NB / NW;        // DMA per wavefront
   __shared__ u32x4_t la0[NA * 64], la1[NA * 64], la2[NA * 64], la3[NA * 64];
   __shared__ u32x4_t lb0[NB * 64], lb1[NB * 64], lb2[NB * 64], lb3[NB * 64];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / WN, wn = w % WN;
   const int c16 = lane & 15, q = lane >> 4;
   const int c32 = lane & 31, hi = (lane >> 4) & 1, ks = lane >> 5;
   const int K = a.K, KB = K / 32, KT = K / 32;
@@ -82,12 +88,12 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GArgs a) {
     const int4 td = a.tiles[tile];
     const int g = td.x, row0 = td.y, nrows = td.z;
     const bool sh = g == a.P;
-    // this wavefront stages A row blocks w + 4h and B column blocks w + 4h
+    // this wavefront stages A row blocks w + NW h and B column blocks w + NW h
     const bf16_t* ga[HA];
     const u32x4_t* gb[HB];
 #pragma unroll
     for (int h = 0; h < HA; ++h) {
-      const int mb = w + 4 * h;
+      const int mb = w + NW * h;
       int r = mb * 16 + c16;
       if (r >= nrows) r = 0;               // padded rows read row 0, unused
       const int rr = row0 + r;
@@ -97,18 +103,23 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GArgs a) {
     }
 #pragma unroll
     for (int h = 0; h < HB; ++h) {
-      const int cb = w + 4 * h;
-      // column blocks [0, NB/2) are gate, the rest up, of the same outputs
-      const void* W = cb < NB / 2 ? (sh ? a.w0_sh : a.w0_arr[g])
-                                  : (sh ? a.w1_sh : a.w1_arr[g]);
-      const int nb16 = nb * (NB / 2) + (cb < NB / 2 ? cb : cb - NB / 2);
+      const int cb = w + NW * h;
+      const void* W;
+      int nb16;
+      if (MODE == G_GATEUP) {   // blocks [0, NB/2) gate, the rest up, same outputs
+        W = cb < NB / 2 ? (sh ? a.w0_sh : a.w0_arr[g]) : (sh ? a.w1_sh : a.w1_arr[g]);
+        nb16 = nb * (NB / 2) + (cb < NB / 2 ? cb : cb - NB / 2);
+      } else {
+        W = sh ? a.w0_sh : a.w0_arr[g];
+        nb16 = nb * NB + cb;
+      }
       gb[h] = (const u32x4_t*)W + (size_t)nb16 * KB * 64 + lane;
     }
     auto issue = [&](int kt, u32x4_t* A, u32x4_t* B) {
 #pragma unroll
-      for (int h = 0; h < HA; ++h) lds_dma16(ga[h] + kt * 32, A + (w + 4 * h) * 64);
+      for (int h = 0; h < HA; ++h) lds_dma16(ga[h] + kt * 32, A + (w + NW * h) * 64);
 #pragma unroll
-      for (int h = 0; h < HB; ++h) lds_dma16(gb[h] + (size_t)kt * 64, B + (w + 4 * h) * 64);
+      for (int h = 0; h < HB; ++h) lds_dma16(gb[h] + (size_t)kt * 64, B + (w + NW * h) * 64);
     };
     f32x16_t acc[TM][TN];
 #pragma unroll
@@ -123,9 +134,11 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GArgs a) {
         u32x4_t fb[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          // 32-column block of B: j < TN/2 gate, else the matching up block
-          const int cb32 = (j < TN / 2) ? wn * (TN / 2) + j
-                                        : NB / 4 + wn * (TN / 2) + (j - TN / 2);
+          // 32-column block of B (gate/up: j < TN/2 gate, else the matching
+          // up block)
+          const int cb32 = MODE == G_DOWN ? wn * TN + j
+                           : (j < TN / 2) ? wn * (TN / 2) + j
+                                          : NB / 4 + wn * (TN / 2) + (j - TN / 2);
           fb[j] = B[(2 * cb32 + hi) * 64 + pos];
         }
 #pragma unroll
@@ -169,12 +182,18 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int lr = wm * TM * 32 + i * 32 + 8 * (r >> 2) + 4 * ks + (r & 3);
         if (lr >= nrows) continue;
-        const size_t hr = (size_t)(sh ? a.cap : 0) + row0 + lr;
+        if (MODE == G_GATEUP) {
+          const size_t hr = (size_t)(sh ? a.cap : 0) + row0 + lr;
 #pragma unroll
-        for (int jj = 0; jj < TN / 2; ++jj) {
-          const int n = nb * (NB / 2) * 16 + (wn * (TN / 2) + jj) * 32 + c32;
-          a.h_out[hr * a.N + n] =
-              f32_to_bf16(silu_f32(acc[i][jj][r]) * acc[i][TN / 2 + jj][r]);
+          for (int jj = 0; jj < TN / 2; ++jj) {
+            const int n = nb * (NB / 2) * 16 + (wn * (TN / 2) + jj) * 32 + c32;
+            a.h_out[hr * a.N + n] =
+                f32_to_bf16(silu_f32(acc[i][jj][r]) * acc[i][TN / 2 + jj][r]);
+          }
+        } else {
+          float* y = (sh ? a.y_shared : a.y_routed) + (size_t)(row0 + lr) * a.N;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) y[nb * NB * 16 + (wn * TN + j) * 32 + c32] = acc[i][j][r];
         }
       }
     }
@@ -183,8 +202,12 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GArgs a) {
 
 // Wavefront tile of 4 x 4 blocks of 32 x 32: 256 x 256 workgroup tiles with
 // 128 KiB of LDS (one workgroup per CU).
-static constexpr int kGemmT = 4;
-static constexpr int kGemmRows = 64 * kGemmT;
+// 256 x 256 tiles from 2 x 4 wavefronts of 4 x 2 blocks: two wavefronts per
+// SIMD, so one's barrier or LDS wait is covered by the other's MFMAs (one
+// wavefront per SIMD with 4 x 4 blocks each ran gate/up 17 % slower).
+static constexpr int kGemmWM = 2, kGemmWN = 4;
+static constexpr int kGemmTM = 4, kGemmTN = 2;
+static constexpr int kGemmRows = 32 * kGemmTM * kGemmWM;
 int gemm_tile_rows() { return kGemmRows; }
 
 hipError_t launch_gemm_bf16_gateup(const FfnArgs& f, hipStream_t s) {
@@ -204,9 +227,34 @@ hipError_t launch_gemm_bf16_gateup(const FfnArgs& f, hipStream_t s) {
   a.w0_sh = w->sh_gate;
   a.w1_sh = w->sh_up;
   a.h_out = (bf16_t*)f.h;
-  a.nb_per_tile = a.N / (32 * kGemmT);   // 64*T B-columns = 32*T outputs
+  a.nb_per_tile = a.N / (16 * kGemmTN * kGemmWN);  // 32 TN WN B-columns
   // persistent: one workgroup per CU (128 KiB of LDS, 512 VGPRs a lane)
-  k_gemm_bf16<kGemmT, kGemmT><<<256, 256, 0, s>>>(a);
+  k_gemm_bf16<G_GATEUP, kGemmTM, kGemmTN, kGemmWM, kGemmWN>
+      <<<256, 64 * kGemmWM * kGemmWN, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_down(const FfnArgs& f, hipStream_t s) {
+  const moe_weights* w = f.w;
+  GArgs a{};
+  a.tiles = f.tiles;
+  a.tile_count = f.tile_count;
+  a.P = f.P;
+  a.cap = f.cap;
+  a.K = f.I;
+  a.N = f.H;
+  a.a_routed = (const bf16_t*)f.h;
+  a.a_rows = nullptr;
+  a.a_shared = (const bf16_t*)f.h + (size_t)f.cap * f.I;
+  a.w0_arr = w->w_down;
+  a.w1_arr = nullptr;
+  a.w0_sh = w->sh_down;
+  a.w1_sh = nullptr;
+  a.y_routed = f.y_routed;
+  a.y_shared = f.y_shared;
+  a.nb_per_tile = a.N / (32 * kGemmTN * kGemmWN);  // 32 TN WN outputs
+  k_gemm_bf16<G_DOWN, kGemmTM, kGemmTN, kGemmWM, kGemmWN>
+      <<<256, 64 * kGemmWM * kGemmWN, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -61,6 +61,8 @@ def sample_tokens(T, n, seed=0):
     ("prefill", dict(T=50, H=512, I=256, E=64, num_local=16, k=4)),  # stream
     ("decode", dict(T=64, H=384, I=256, E=32, num_local=8, k=4)),    # stream
     ("decode", dict(T=700, H=256, I=384, E=8, num_local=8, k=2)),    # tiled
+    # ring GEMM gate/up, 128 x 128 tiled down (H not a multiple of 256)
+    ("prefill", dict(T=400, H=384, I=256, E=8, num_local=8, k=2)),
 ])
 def test_layer_reduced_shapes(name, kw):
     wl = make_workload(name, seed=11, **kw)
