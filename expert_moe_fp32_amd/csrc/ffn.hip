@@ -145,9 +145,12 @@ __device__ __forceinline__ void store_block(const KArgs& a, bool sh, int row0,
 }
 
 // ---------------------------------------------- weight-streaming kernel
-// Workgroup = 4 wavefronts = 64 output columns; wavefront w streams packed
-// row block nb*4 + w (16 channels) over the whole reduction; a tile has up to
-// 16*NMB rows.  K chunk = 128 (4 MFMA steps), prefetched one chunk ahead.
+// Workgroup = 4 wavefronts; wavefront w streams two packed row blocks (16
+// channels each) over the whole reduction: gate and up of block nb*4 + w
+// (64 outputs an item), or down blocks nb*8 + w and nb*8 + w + 4 (128
+// outputs an item), so every wavefront keeps two weight streams in flight.
+// A tile has up to 16*NMB rows.  K chunk = 128 (4 MFMA steps), prefetched
+// one chunk ahead.
 template <int MODE, int NMB>
 __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -160,12 +163,13 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
     const int4 td = a.tiles[tile];
     const int g = td.x, row0 = td.y, nrows = td.z;
     const bool sh = g == a.P;
-    const int nb16 = nb * 4 + wv;
+    const int nb16 = MODE == MODE_GATEUP ? nb * 4 + wv : nb * 8 + wv;
     const u32x4_t* b0p = (const u32x4_t*)(sh ? a.w0_sh : a.w0_arr[g]) +
                          (size_t)nb16 * KB * 64 + lane;
-    const u32x4_t* b1p = b0p;
-    if (MODE == MODE_GATEUP)
-      b1p = (const u32x4_t*)(sh ? a.w1_sh : a.w1_arr[g]) + (size_t)nb16 * KB * 64 + lane;
+    const u32x4_t* b1p =
+        MODE == MODE_GATEUP
+            ? (const u32x4_t*)(sh ? a.w1_sh : a.w1_arr[g]) + (size_t)nb16 * KB * 64 + lane
+            : b0p + (size_t)4 * KB * 64;        // down: the block 64 channels on
     const bf16_t* ap[NMB];
     bool av[NMB];
 #pragma unroll
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       b0c[s] = load_nt(b0p + s * 64);
-      if (MODE == MODE_GATEUP) b1c[s] = load_nt(b1p + s * 64);
+      b1c[s] = load_nt(b1p + s * 64);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
         acur[mb][s] = av[mb] ? *(const u32x4_t*)(ap[mb] + 32 * s) : zero;
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           b0n[s] = load_nt(b0p + (kb + s) * 64);
-          if (MODE == MODE_GATEUP) b1n[s] = load_nt(b1p + (kb + s) * 64);
+          b1n[s] = load_nt(b1p + (kb + s) * 64);
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb)
             anext[mb][s] = av[mb] ? *(const u32x4_t*)(ap[mb] + k0 + 128 + 32 * s) : zero;
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
         for (int mb = 0; mb < NMB; ++mb) {
           if (mb < nmb) {
             acc0[mb] = mfma16(acur[mb][s], b0c[s], acc0[mb]);
-            if (MODE == MODE_GATEUP) acc1[mb] = mfma16(acur[mb][s], b1c[s], acc1[mb]);
+            acc1[mb] = mfma16(acur[mb][s], b1c[s], acc1[mb]);
           }
         }
       }
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           b0c[s] = b0n[s];
-          if (MODE == MODE_GATEUP) b1c[s] = b1n[s];
+          b1c[s] = b1n[s];
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) acur[mb][s] = anext[mb][s];
         }
@@ -227,8 +231,12 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
     }
     const int n = nb16 * 16 + c16;
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-      if (mb < nmb) store_block<MODE>(a, sh, row0, nrows, mb * 16, n, acc0[mb], acc1[mb]);
+    for (int mb = 0; mb < NMB; ++mb) {
+      if (mb >= nmb) continue;
+      store_block<MODE>(a, sh, row0, nrows, mb * 16, n, acc0[mb], acc1[mb]);
+      if (MODE == MODE_DOWN)
+        store_block<MODE>(a, sh, row0, nrows, mb * 16, n + 64, acc1[mb], acc1[mb]);
+    }
   }
 }
 
@@ -533,7 +541,7 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
     if (grid > cu * 8) grid = cu * 8;
     k_f32<MODE_DOWN><<<(unsigned)grid, 256, 0, s>>>(a);
   } else if (stream) {
-    a.nb_per_tile = a.N / 64;
+    a.nb_per_tile = a.N / 128;                // two 64-apart blocks per wave
     long items = max_tiles * a.nb_per_tile;
     long grid = items < cu * 16 ? items : cu * 16;
     k_stream_bf16<MODE_DOWN, 2><<<(unsigned)grid, 256, 0, s>>>(a);

@@ -325,9 +325,16 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
     const u32x4_t* wp1 = (const u32x4_t*)W1 + (size_t)cb1 * KB * 128 + lane;
     // dump-slot source: 256 contiguous bytes of the column's own block
     const float* sdump = (const float*)((const u32x4_t*)W0 + (size_t)cb0 * KB * 128) + lane;
-    // weight scales, one K block per lane (two registers cover KB <= 128)
-    const float* sc0 = S0 + (size_t)(cb0 >> 3) * KB;
-    const float* sc1 = S1 + (size_t)(cb1 >> 3) * KB;
+    // Compute layout: wavefront (wr, wc) = (wv / 4, wv % 4) takes row blocks
+    // [wr MH, wr MH + MH) and four of the stage's 16 weight blocks -- gate
+    // and up of channel blocks 2 wc, 2 wc + 1, or down blocks 4 wc .. 4 wc + 3
+    // -- so each activation fragment feeds 4 MFMAs and each weight fragment
+    // MH.  Its weight scales (one 128-channel scale block per matrix), one K
+    // block per lane (two registers cover KB <= 128):
+    const int wr = wv >> 2, wc = wv & 3;
+    const float* sc0 = MODE == M8_GATEUP ? S0 + (size_t)nb * KB
+                                         : S0 + (size_t)(2 * nb + (wc >> 1)) * KB;
+    const float* sc1 = MODE == M8_GATEUP ? S1 + (size_t)nb * KB : sc0;
     const float w0lo = lane < KB ? sc0[lane] : 0.f;
     const float w0hi = lane + 64 < KB ? sc0[lane + 64] : 0.f;
     const float w1lo = lane < KB ? sc1[lane] : 0.f;
@@ -353,33 +360,42 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
       __builtin_amdgcn_global_load_lds(sg, (lds_void*)(S + 64 * (sreal ? wv : NRS)),
                                        4, 0, 0);
     };
-    f32x4_t acc0[NMB], acc1[NMB];
+    constexpr int MH = NMB / 2;                  // row blocks per wavefront
+    // the stage's weight slot of this wavefront's block j (DMA order: slot s
+    // < 8 gate / down block s, slot 8 + s up / down block 8 + s)
+    auto bslot = [&](int j) -> int {
+      return MODE == M8_GATEUP ? (j < 2 ? 2 * wc + j : 8 + 2 * wc + (j - 2)) : 4 * wc + j;
+    };
+    f32x4_t acc[MH][4];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      acc0[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      acc1[mb] = acc0[mb];
-    }
-    // All NMB row blocks run, straight-line, whatever nrows is: the MFMAs
+    for (int m = 0; m < MH; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // All MH row blocks run, straight-line, whatever nrows is: the MFMAs
     // are cheap next to the weight stream, and a branch per block would
     // make every block wait out its own LDS latency.  Padded rows hold row
     // 0's data and are never stored.
     auto compute = [&](int kb, const u32x4_t* A, const u32x4_t* B, const float* S) {
       const float ws0 = wscale(w0lo, w0hi, kb);
-      const float ws1 = wscale(w1lo, w1hi, kb);
-      const i32x8_t fb0 = join(B[wv * 128 + lane], B[wv * 128 + 64 + lane]);
-      const i32x8_t fb1 = join(B[(8 + wv) * 128 + lane], B[(8 + wv) * 128 + 64 + lane]);
+      const float ws1 = MODE == M8_GATEUP ? wscale(w1lo, w1hi, kb) : ws0;
+      i32x8_t fb[4];
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
+      for (int j = 0; j < 4; ++j)
+        fb[j] = join(B[bslot(j) * 128 + lane], B[bslot(j) * 128 + 64 + lane]);
+#pragma unroll
+      for (int m = 0; m < MH; ++m) {
+        const int mb = wr * MH + m;
         const i32x8_t fa = join(A[mb * 128 + lane], A[mb * 128 + 64 + lane]);
         const f32x4_t sa = *(const f32x4_t*)(S + mb * 16 + 4 * q);
-        const f32x4_t p0 = mfma_fp8(fa, fb0);
-        const f32x4_t p1 = mfma_fp8(fa, fb1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc0[mb][r] = __builtin_fmaf(p0[r], sa[r] * ws0, acc0[mb][r]);
-          acc1[mb][r] = __builtin_fmaf(p1[r], sa[r] * ws1, acc1[mb][r]);
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t p = mfma_fp8(fa, fb[j]);
+          const float ws = (MODE == M8_GATEUP && j >= 2) ? ws1 : ws0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[m][j][r] = __builtin_fmaf(p[r], sa[r] * ws, acc[m][j][r]);
         }
-        if ((mb & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound hoisting
+        if ((m & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound hoisting
       }
     };
     lds_barrier();                               // last item done with the ring
@@ -405,7 +421,8 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
     }
     WAIT_VMCNT(0);                               // trailing re-reads landed
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
+    for (int m = 0; m < MH; ++m) {
+      const int mb = wr * MH + m;
       if (mb >= nmb) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -413,11 +430,14 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
         if (lr >= nrows) continue;
         if (MODE == M8_GATEUP) {
           const size_t hr = (size_t)(sh ? a.cap : 0) + row0 + lr;
-          a.h_out[hr * a.N + cb0 * 16 + c16] = silu_f32(acc0[mb][r]) * acc1[mb][r];
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            a.h_out[hr * a.N + (nb * 8 + 2 * wc + j) * 16 + c16] =
+                silu_f32(acc[m][j][r]) * acc[m][2 + j][r];
         } else {
           float* y = (sh ? a.y_shared : a.y_routed) + (size_t)(row0 + lr) * a.N;
-          y[cb0 * 16 + c16] = acc0[mb][r];
-          y[cb1 * 16 + c16] = acc1[mb][r];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[(nb * 16 + 4 * wc + j) * 16 + c16] = acc[m][j][r];
         }
       }
     }
