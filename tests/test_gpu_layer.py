@@ -132,3 +132,40 @@ def test_full_skewed_with_and_without_replicas(skewed):
     base = ref.disp.logical_counts
     print(f"  busiest/mean local expert: a {base.max() / base.mean():.2f}, "
           f"b {ref.disp.phys_counts.max() / ref.disp.phys_counts.mean():.2f}")
+
+
+def with_hot_expert(wl, e):
+    """Every token gets local expert e in its top-k (its logit raised by 20):
+    one expert holds all T rows, several tiles of them."""
+    logits = wl.logits.copy()
+    logits[:, e] += 20.0
+    wl._cache["logits"] = logits
+    return wl
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("prefill", dict(T=600, H=256, I=256, E=16, num_local=8, k=4)),  # ring GEMM
+    ("decode", dict(T=64, H=384, I=256, E=32, num_local=8, k=4)),    # stream
+    ("fp8", dict(T=400, H=512, I=1024, E=16, num_local=8, k=4)),     # FP8 ring
+])
+def test_layer_hot_expert(name, kw):
+    wl = with_hot_expert(make_workload(name, seed=17, **kw), 3)
+    print(f"layer hot expert 3: {wl.describe()}", flush=True)
+    out, counts = run_layer(wl)
+    ref = oracle_out(wl)
+    assert counts[3] == wl.T
+    assert np.array_equal(counts, ref.counts)
+    check_output(out, ref.out, wl.out, BARS[recipe(wl)], wl.describe())
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("decode", dict(T=1, H=384, I=256, E=32, num_local=8, k=4)),
+    ("prefill", dict(T=1, H=256, I=256, E=16, num_local=8, k=4)),   # + shared
+    ("fp8", dict(T=1, H=512, I=512, E=16, num_local=8, k=4)),
+])
+def test_layer_single_token(name, kw):
+    wl = make_workload(name, seed=19, **kw)
+    print(f"layer {wl.describe()}", flush=True)
+    out, _ = run_layer(wl)
+    ref = oracle_out(wl)
+    check_output(out, ref.out, wl.out, BARS[recipe(wl)], wl.describe())
