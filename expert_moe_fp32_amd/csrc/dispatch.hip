@@ -121,10 +121,16 @@ __global__ __launch_bounds__(1024) void k_scan(
   __syncthreads();
   for (int e = threadIdx.x; e < L; e += blockDim.x) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = block_counts[(size_t)b * L + e];
-      block_base[(size_t)b * L + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += 8) {     // eight loads in flight
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        c[u] = b0 + u < nblk ? block_counts[(size_t)(b0 + u) * L + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b0 + u < nblk) block_base[(size_t)(b0 + u) * L + e] = run;
+        run += c[u];
+      }
     }
     const int R = rep ? min(max(rep[e], 1), max_rep) : 1;
     for (int r = 0; r < R; ++r) {
@@ -218,11 +224,14 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
   for (int i = t; i <= P; i += 1024) pc[i] = 0;
   __syncthreads();
   int le[MOE_KMAX];
+  float wj[MOE_KMAX];                      // route weights, loaded with the ids
 #pragma unroll
   for (int j = 0; j < MOE_KMAX; ++j) {
     le[j] = -1;
+    wj[j] = 0.0f;
     if (j < k && t < T) {
       const int gid = a.ids[(size_t)t * k + j];
+      wj[j] = a.w[(size_t)t * k + j];
       atomicAdd(&cnt[gid], 1);
       const int e = gid - a.expert_begin;
       if (e >= 0 && e < L) le[j] = e;
@@ -324,7 +333,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
     const int row = pc[p] + n / R;
     a.pair_row[o] = row;
     a.row_token[row] = t;
-    a.row_weight[row] = a.w[o];
+    a.row_weight[row] = wj[j];
   }
 }
 
