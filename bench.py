@@ -52,21 +52,24 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 # and the tables).  The figures hold for the kernel source they were taken
 # on: when the SHA-256 of its files differs, traffic is reported as null.
 TRAFFIC = {
-    "decode": dict(kernel="k_stream_bf16<0, 2>",
-                   files=("expert_moe_fp32_amd/csrc/ffn.hip",
-                          "expert_moe_fp32_amd/csrc/common.h"),
-                   sha="9fc2192c5d0f462a", fetch_kib=794481.0, write_kib=988.3,
-                   fetch_factor=1.9977, write_factor=1.0),
-    "prefill": dict(kernel="k_gemm_bf16<4, 4>",
-                    files=("expert_moe_fp32_amd/csrc/gemm_bf16.hip",
-                           "expert_moe_fp32_amd/csrc/common.h"),
-                    sha="9fd786ff6a12c7ae", fetch_kib=2166375.0,
-                    write_kib=106888.0, fetch_factor=1.998, write_factor=1.0),
-    "fp8": dict(kernel="k_ring_fp8<0, 10>",
-                files=("expert_moe_fp32_amd/csrc/ffn_fp8.hip",
-                       "expert_moe_fp32_amd/csrc/common.h"),
-                sha="ab485ca6ee1357c3", fetch_kib=474027.7, write_kib=33232.0,
-                fetch_factor=1.9956, write_factor=1.0),
+    "decode": dict(
+        kernel="k_stream_bf16<0, 2>",
+        files=("expert_moe_fp32_amd/csrc/ffn.hip",
+               "expert_moe_fp32_amd/csrc/common.h"),
+        sha="9b38c047aa85acc7", fetch_kib=794473.7, write_kib=988.3,
+        fetch_factor=1.9969, write_factor=1.0),
+    "prefill": dict(
+        kernel="k_gemm_bf16<0, 4, 2, 2, 4>",
+        files=("expert_moe_fp32_amd/csrc/gemm_bf16.hip",
+               "expert_moe_fp32_amd/csrc/common.h"),
+        sha="9231f8118f172206", fetch_kib=2386616.0, write_kib=88744.2,
+        fetch_factor=1.9973, write_factor=1.0),
+    "fp8": dict(
+        kernel="k_ring_fp8<0, 10>",
+        files=("expert_moe_fp32_amd/csrc/ffn_fp8.hip",
+               "expert_moe_fp32_amd/csrc/common.h"),
+        sha="879a9b856507e02d", fetch_kib=473973.2, write_kib=33232.0,
+        fetch_factor=1.9956, write_factor=1.0),
 }
 
 
