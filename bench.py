@@ -56,7 +56,7 @@ TRAFFIC = {
         kernel="k_stream_bf16<0, 2>",
         files=("expert_moe_fp32_amd/csrc/ffn.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="9b38c047aa85acc7", fetch_kib=794473.7, write_kib=988.3,
+        sha="04e6a8e1e7ebc214", fetch_kib=794479.3, write_kib=988.3,
         fetch_factor=1.9969, write_factor=1.0),
     "prefill": dict(
         kernel="k_gemm_bf16<0, 4, 2, 2, 4>",

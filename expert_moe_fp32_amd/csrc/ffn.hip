@@ -25,7 +25,7 @@
 //    is read once per tile.
 //  * k_gemm_bf16 (gemm_bf16.hip; groups of hundreds of rows, prefill): the
 //    256 x 256 LDS-ring GEMM for gate/up and down.
-//  * k_tile_bf16: 128 rows x 128 columns per workgroup, double-buffered LDS
+//  * k_tile_bf16_down: 128 rows x 128 columns per workgroup, double-buffered LDS
 //    holding operand blocks in lane order (conflict-free 16-B reads, no
 //    padding), 2x2 wavefronts of 64 x 64; the down pass when H is not a
 //    multiple of 256.
@@ -241,16 +241,14 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
 }
 
 // ----------------------------------------------------- LDS-tiled kernel
-// Tile: 128 rows x 128 B-columns (gate/up: 64 gate + 64 up channels of the
-// same 64 outputs; down: 128 outputs), BK = 64 (two MFMA steps).  LDS holds,
+// Down tile: 128 rows x 128 outputs, BK = 64 (two MFMA steps).  LDS holds,
 // per stage, the A operand as 8 row blocks x 2 steps and the B operand as
 // 8 column blocks x 2 steps, each a 1 KiB lane-ordered block, so every
 // fragment read is one conflict-free ds_read_b128 at lane * 16 bytes.
 // Wavefront (wm, wn) of a 2x2 grid owns 64 rows x 64 B-columns.
 static constexpr int TBM = 128, TBK = 64;
 
-template <int MODE>
-__global__ __launch_bounds__(256) void k_tile_bf16(KArgs a) {
+__global__ __launch_bounds__(256) void k_tile_bf16_down(KArgs a) {
   __shared__ u32x4_t lds_a[2][16 * 64];
   __shared__ u32x4_t lds_b[2][16 * 64];
   const int tid = threadIdx.x;
@@ -278,16 +276,8 @@ __global__ __launch_bounds__(256) void k_tile_bf16(KArgs a) {
       va[j] = r < nrows;
       ga[j] = a_row(a, sh, row0 + (va[j] ? r : 0)) + (blk & 1) * 32 + (lane >> 4) * 8;
       const int cb = blk >> 1;           // local column block 0..7
-      const u32x4_t* W;
-      int nb16;
-      if (MODE == MODE_GATEUP) {         // blocks 0..3 gate, 4..7 up
-        W = (const u32x4_t*)(cb < 4 ? (sh ? a.w0_sh : a.w0_arr[g])
-                                    : (sh ? a.w1_sh : a.w1_arr[g]));
-        nb16 = nb * 4 + (cb & 3);
-      } else {
-        W = (const u32x4_t*)(sh ? a.w0_sh : a.w0_arr[g]);
-        nb16 = nb * 8 + cb;
-      }
+      const u32x4_t* W = (const u32x4_t*)(sh ? a.w0_sh : a.w0_arr[g]);
+      const int nb16 = nb * 8 + cb;
       gb[j] = W + ((size_t)nb16 * KB + (blk & 1)) * 64 + lane;
     }
     u32x4_t ra[4], rb[4];
@@ -326,12 +316,7 @@ __global__ __launch_bounds__(256) void k_tile_bf16(KArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) fa[i] = lds_a[cur][((wm * 4 + i) * 2 + s) * 64 + lane];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int cb;
-          if (MODE == MODE_GATEUP) cb = (j >> 1) * 4 + wn * 2 + (j & 1);
-          else cb = wn * 4 + j;
-          fb[j] = lds_b[cur][(cb * 2 + s) * 64 + lane];
-        }
+        for (int j = 0; j < 4; ++j) fb[j] = lds_b[cur][((wn * 4 + j) * 2 + s) * 64 + lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (i < nmb_valid)
@@ -352,18 +337,10 @@ __global__ __launch_bounds__(256) void k_tile_bf16(KArgs a) {
     for (int i = 0; i < 4; ++i) {
       if (i >= nmb_valid) continue;
       const int rbase = wm * 64 + i * 16;
-      if (MODE == MODE_GATEUP) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = nb * 64 + wn * 32 + j * 16 + c16;
-          store_block<MODE>(a, sh, row0, nrows, rbase, n, acc[i][j], acc[i][j + 2]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = nb * 128 + wn * 64 + j * 16 + c16;
-          store_block<MODE>(a, sh, row0, nrows, rbase, n, acc[i][j], acc[i][j]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int n = nb * 128 + wn * 64 + j * 16 + c16;
+        store_block<MODE_DOWN>(a, sh, row0, nrows, rbase, n, acc[i][j], acc[i][j]);
       }
     }
   }
@@ -557,7 +534,7 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
     const long tiles_down = ring ? G + hrows / TBM + 1 : max_tiles;
     long items = tiles_down * a.nb_per_tile;
     long grid = items < cu * 2 ? items : cu * 2;
-    k_tile_bf16<MODE_DOWN><<<(unsigned)grid, 256, 0, s>>>(a);
+    k_tile_bf16_down<<<(unsigned)grid, 256, 0, s>>>(a);
   }
   if (f.events) hipEventRecord(f.events[2], s);
   return hipGetLastError();
