@@ -6,12 +6,14 @@
 // A workgroup of 8 wavefronts (2 x 4) computes 256 x 256 B-columns:
 // wavefront (wm, wn) owns 128 rows x 64 columns = 4 x 2 MFMA blocks of
 // 32 x 32 (128 fp32 accumulators per lane, two wavefronts per SIMD).  The
-// reduction runs in 32-wide stages held in a ring of 4 LDS stages; each stage
-// is 16 A blocks + 16 B blocks of 1 KiB in lane order, filled by
-// global_load_lds_dwordx4 (each lane's 16 bytes land at block base + 16 *
-// lane, so no registers stage the copy and every fragment read is one
-// conflict-free ds_read_b128).  Loads run three stages ahead of the MFMAs;
-// one barrier per stage.
+// reduction runs in 32-wide stages through LDS filled by
+// global_load_lds_dwordx4 (each lane's 16 bytes land at the transfer's base
+// + 16 * lane, so no registers stage the copy): B in a ring of 4 stages of 16
+// column blocks of 1 KiB, A in 2 slots of a stage pair, where one transfer
+// moves 8 whole 128-byte row segments (64 K) -- a transfer of 16 rows x 64
+// bytes, half a cache line per row, ran the loop about 14 % slower.  Every
+// fragment read is one conflict-free ds_read_b128; one barrier per stage,
+// loads two to three stages ahead of the MFMAs.
 //
 // Placement: workgroups are dealt round-robin to the 8 XCDs (workgroup b on
 // XCD b % 8).  Items are numbered column block fastest, so consecutive items
@@ -57,24 +59,26 @@ __device__ __forceinline__ f32x16_t mfma32b(u32x4_t a, u32x4_t b, f32x16_t c) {
 // Workgroup = WM x WN wavefronts; wavefront (wm, wn) owns TM x TN blocks of
 // 32 x 32 computed with v_mfma_f32_32x32x16_bf16 (on gfx950 this instruction
 // sustains about 1.6x the rate of the 16x16x32 form), so a tile is
-// 32*TM*WM rows x 32*TN*WN B-columns.  Ring of 4 LDS stages of 32-wide K, each holding the
-// tile's 16 x 32 operand blocks (1 KiB, lane order) as staged by
-// global_load_lds.  A 32 x 16 MFMA operand is read from two vertically
-// adjacent blocks: lane l takes row l % 32 (block (l % 32) / 16, its row
-// l % 16) and K-slot 2s + l / 32 of the stage's 32-wide K (substep s = 0, 1):
-// 16 lanes read 256 contiguous bytes, conflict-free.  The accumulator of lane
-// l holds column l % 32 and rows 8 * (r / 4) + 4 * (l / 32) + r % 4, r < 16.
+// 32*TM*WM rows x 32*TN*WN B-columns.  B stages hold the tile's 16-column x
+// 32-K blocks (1 KiB, lane order): a 16 x 32 B operand is read from two
+// adjacent blocks, lane l taking column l % 32 (block (l % 32) / 16, its
+// column l % 16) and K-slot 2s + l / 32 of the stage (substep s = 0, 1), so
+// 16 lanes read 256 contiguous bytes.  A pair slots hold 8-row blocks laid
+// out as described at the staging code; lane l reads row l % 32 and the same
+// K-slot.  The accumulator of lane l holds column l % 32 and rows
+// 8 * (r / 4) + 4 * (l / 32) + r % 4, r < 16.
 template <int MODE, int TM, int TN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
   constexpr int NW = WM * WN;                      // wavefronts
-  constexpr int NA = 2 * TM * WM, NB = 2 * TN * WN;  // 16-wide blocks per stage
-  constexpr int HA = NA / NW, HB = NB / NW;        // DMA per wavefront
-  __shared__ u32x4_t la0[NA * 64], la1[NA * 64], la2[NA * 64], la3[NA * 64];
+  constexpr int NR8 = 4 * TM * WM;                 // 8-row A blocks per tile
+  constexpr int NB = 2 * TN * WN;                  // 16-column B blocks per stage
+  constexpr int HA = NR8 / NW, HB = NB / NW;       // DMA per wavefront: A per pair, B per stage
+  __shared__ u32x4_t pa0[NR8 * 64], pa1[NR8 * 64];   // A: two slots of a stage pair
   __shared__ u32x4_t lb0[NB * 64], lb1[NB * 64], lb2[NB * 64], lb3[NB * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / WN, wn = w % WN;
-  const int c16 = lane & 15, q = lane >> 4;
+  const int c16 = lane & 15;
   const int c32 = lane & 31, hi = (lane >> 4) & 1, ks = lane >> 5;
   const int K = a.K, KB = K / 32, KT = K / 32;
   const int total = a.tile_count[0] * a.nb_per_tile;
@@ -88,18 +92,23 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
     const int4 td = a.tiles[tile];
     const int g = td.x, row0 = td.y, nrows = td.z;
     const bool sh = g == a.P;
-    // this wavefront stages A row blocks w + NW h and B column blocks w + NW h
+    // This wavefront stages A blocks w + NW h (8 rows of a stage pair) and
+    // B column blocks w + NW h.  An A transfer takes 128 contiguous bytes
+    // (64 K) of each of 8 rows: lane i loads row 8b + (i & 7), stage i >> 5
+    // of the pair, 8-element chunk c = ((i >> 3) & 3) ^ (b & 1), and lands
+    // at 16 i, so a block holds the pair's first stage in its first 512
+    // bytes and its second in the rest, each as [chunk slot][row].
     const bf16_t* ga[HA];
     const u32x4_t* gb[HB];
 #pragma unroll
     for (int h = 0; h < HA; ++h) {
-      const int mb = w + NW * h;
-      int r = mb * 16 + c16;
+      const int b8 = w + NW * h;
+      int r = b8 * 8 + (lane & 7);
       if (r >= nrows) r = 0;               // padded rows read row 0, unused
       const int rr = row0 + r;
       const bf16_t* rowp = sh ? a.a_shared + (size_t)rr * K
                               : a.a_routed + (size_t)(a.a_rows ? a.a_rows[rr] : rr) * K;
-      ga[h] = rowp + 8 * q;
+      ga[h] = rowp + (lane >> 5) * 32 + ((((lane >> 3) & 3) ^ (b8 & 1)) * 8);
     }
 #pragma unroll
     for (int h = 0; h < HB; ++h) {
@@ -115,9 +124,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
       }
       gb[h] = (const u32x4_t*)W + (size_t)nb16 * KB * 64 + lane;
     }
-    auto issue = [&](int kt, u32x4_t* A, u32x4_t* B) {
+    auto issue_a = [&](int kp, u32x4_t* A) {     // stages 2 kp and 2 kp + 1
 #pragma unroll
-      for (int h = 0; h < HA; ++h) lds_dma16(ga[h] + kt * 32, A + (w + NW * h) * 64);
+      for (int h = 0; h < HA; ++h) lds_dma16(ga[h] + kp * 64, A + (w + NW * h) * 64);
+    };
+    auto issue_b = [&](int kt, u32x4_t* B) {
 #pragma unroll
       for (int h = 0; h < HB; ++h) lds_dma16(gb[h] + (size_t)kt * 64, B + (w + NW * h) * 64);
     };
@@ -127,10 +138,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
     const int valid_rows = nrows - wm * TM * 32;   // may be <= 0
-    auto compute = [&](const u32x4_t* A, const u32x4_t* B) {
+    // stage HH of the pair in slot A: lane l reads row l % 32 of a 32-row
+    // block (8-row block (l % 32) / 8, its row l % 8), chunk 2 s + l / 32 at
+    // chunk slot chunk ^ ((l >> 3) & 1); the 16 lanes of a read cover two
+    // 128-byte runs in opposite bank halves
+    auto compute = [&](const u32x4_t* A, int HH, const u32x4_t* B) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int pos = c16 + 16 * (2 * s + ks);   // lane slot inside a block
+        const int pos = c16 + 16 * (2 * s + ks);   // lane slot inside a B block
+        const int apos = ((lane & 31) >> 3) * 64 + HH * 32 + (lane & 7) +
+                         8 * ((2 * s + ks) ^ ((lane >> 3) & 1));
         u32x4_t fb[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -143,65 +160,83 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const u32x4_t fa = A[(2 * (wm * TM + i) + hi) * 64 + pos];
+          const u32x4_t fa = A[(wm * TM + i) * 4 * 64 + apos];
 #pragma unroll
           for (int j = 0; j < TN; ++j) acc[i][j] = mfma32b(fa, fb[j], acc[i][j]);
         }
       }
     };
     lds_barrier();                       // previous item done with the ring
-    // prologue: stages 0..2 (KT >= 4)
-    issue(0, la0, lb0);
-    issue(1, la1, lb1);
-    issue(2, la2, lb2);
-    // Main loop, four stages per trip (KT % 4 == 0).  Every step issues one
-    // stage (past the end it re-reads the last stage into a ring slot that is
-    // never read again), so exactly two later stages (HA + HB loads each) are
-    // in flight and "this stage has landed" is one fixed vmcnt at every step.
+    // Ring: B stage k in slot k % 4, A pair k / 2 in slot (k / 2) % 2.  An
+    // even step k issues A pair k / 2 + 1 then B stage k + 3, an odd step B
+    // stage k + 3 (past the end the last pair / stage is re-read into a slot
+    // that is never read again), so the waits are fixed counts: an even step
+    // needs the pair issued two steps back (2 HB younger transfers), an odd
+    // step its B stage (HA + 2 HB younger).  KT % 4 == 0.
+    issue_b(0, lb0);
+    issue_a(0, pa0);
+    issue_b(1, lb1);
+    issue_b(2, lb2);
+    const int last_pair = KT / 2 - 1;
     for (int kt = 0; kt < KT; kt += 4) {
-#define GEMM_STEP(S, AC, BC, AN, BN_)                          \
+#define GEMM_STEP(S, PA, HH, BC, PN, BN_)                      \
       {                                                        \
         const int k = kt + S;                                  \
-        WAIT_VMCNT(2 * (HA + HB));                             \
+        if (S % 2 == 0) WAIT_VMCNT(2 * HB);                    \
+        else WAIT_VMCNT(HA + 2 * HB);                          \
         lds_barrier();                                         \
-        issue(k + 3 < KT ? k + 3 : KT - 1, AN, BN_);           \
-        if (valid_rows > 0) compute(AC, BC);                   \
+        if (S % 2 == 0) issue_a(k / 2 + 1 < last_pair ? k / 2 + 1 : last_pair, PN); \
+        issue_b(k + 3 < KT ? k + 3 : KT - 1, BN_);             \
+        if (valid_rows > 0) compute(PA, HH, BC);               \
       }
-      GEMM_STEP(0, la0, lb0, la3, lb3)
-      GEMM_STEP(1, la1, lb1, la0, lb0)
-      GEMM_STEP(2, la2, lb2, la1, lb1)
-      GEMM_STEP(3, la3, lb3, la2, lb2)
+      GEMM_STEP(0, pa0, 0, lb0, pa1, lb3)
+      GEMM_STEP(1, pa0, 1, lb1, pa1, lb0)
+      GEMM_STEP(2, pa1, 0, lb2, pa0, lb1)
+      GEMM_STEP(3, pa1, 1, lb3, pa0, lb2)
 #undef GEMM_STEP
     }
     WAIT_VMCNT(0);                       // the trailing re-reads have landed
-    // epilogue, one row block at a time
+    // Epilogue, one row block at a time: a wave-uniform 64-bit base per
+    // block and 32-bit lane offsets.  N is read through an opaque move so
+    // the offsets are formed here rather than hoisted out of the item loop
+    // (hoisted, they held registers through the MFMA loop).
+    int N;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(N) : "s"(a.N));
+    const int lane_off = 4 * ks * N + c32;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       __builtin_amdgcn_sched_barrier(0);
+      const int rb = wm * TM * 32 + i * 32;      // the block's first row
+      if (rb >= nrows) break;
+      if (MODE == G_GATEUP) {
+        bf16_t* base = a.h_out + ((size_t)(sh ? a.cap : 0) + row0 + rb) * N +
+                       nb * (NB / 2) * 16 + wn * (TN / 2) * 32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = wm * TM * 32 + i * 32 + 8 * (r >> 2) + 4 * ks + (r & 3);
-        if (lr >= nrows) continue;
-        if (MODE == G_GATEUP) {
-          const size_t hr = (size_t)(sh ? a.cap : 0) + row0 + lr;
+        for (int r = 0; r < 16; ++r) {
+          const int lr = 8 * (r >> 2) + 4 * ks + (r & 3);
+          if (rb + lr >= nrows) continue;
+          const int off = lane_off + (8 * (r >> 2) + (r & 3)) * N;
 #pragma unroll
-          for (int jj = 0; jj < TN / 2; ++jj) {
-            const int n = nb * (NB / 2) * 16 + (wn * (TN / 2) + jj) * 32 + c32;
-            a.h_out[hr * a.N + n] =
+          for (int jj = 0; jj < TN / 2; ++jj)
+            base[off + jj * 32] =
                 f32_to_bf16(silu_f32(acc[i][jj][r]) * acc[i][TN / 2 + jj][r]);
-          }
-        } else {
-          float* y = (sh ? a.y_shared : a.y_routed) + (size_t)(row0 + lr) * a.N;
+        }
+      } else {
+        float* base = (sh ? a.y_shared : a.y_routed) + (size_t)(row0 + rb) * N +
+                      nb * NB * 16 + wn * TN * 32;
 #pragma unroll
-          for (int j = 0; j < TN; ++j) y[nb * NB * 16 + (wn * TN + j) * 32 + c32] = acc[i][j][r];
+        for (int r = 0; r < 16; ++r) {
+          const int lr = 8 * (r >> 2) + 4 * ks + (r & 3);
+          if (rb + lr >= nrows) continue;
+          const int off = lane_off + (8 * (r >> 2) + (r & 3)) * N;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) base[off + j * 32] = acc[i][j][r];
         }
       }
     }
   }
 }
 
-// Wavefront tile of 4 x 4 blocks of 32 x 32: 256 x 256 workgroup tiles with
-// 128 KiB of LDS (one workgroup per CU).
 // 256 x 256 tiles from 2 x 4 wavefronts of 4 x 2 blocks: two wavefronts per
 // SIMD, so one's barrier or LDS wait is covered by the other's MFMAs (one
 // wavefront per SIMD with 4 x 4 blocks each ran gate/up 17 % slower).
@@ -228,7 +263,7 @@ hipError_t launch_gemm_bf16_gateup(const FfnArgs& f, hipStream_t s) {
   a.w1_sh = w->sh_up;
   a.h_out = (bf16_t*)f.h;
   a.nb_per_tile = a.N / (16 * kGemmTN * kGemmWN);  // 32 TN WN B-columns
-  // persistent: one workgroup per CU (128 KiB of LDS, 512 VGPRs a lane)
+  // persistent: one workgroup per CU (128 KiB of LDS)
   k_gemm_bf16<G_GATEUP, kGemmTM, kGemmTN, kGemmWM, kGemmWN>
       <<<256, 64 * kGemmWM * kGemmWN, 0, s>>>(a);
   return hipGetLastError();
