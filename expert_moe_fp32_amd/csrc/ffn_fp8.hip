@@ -374,7 +374,10 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
     // All MH row blocks run, straight-line, whatever nrows is: the MFMAs
     // are cheap next to the weight stream, and a branch per block would
     // make every block wait out its own LDS latency.  Padded rows hold row
-    // 0's data and are never stored.
+    // 0's data and are never stored.  The products of consecutive row blocks
+    // alternate between two register sets and block m + 1's MFMAs issue
+    // before block m's scaling: with one temporary, each MFMA waited for the
+    // previous product's scaling and each scaling for its MFMA's result.
     auto compute = [&](int kb, const u32x4_t* A, const u32x4_t* B, const float* S) {
       const float ws0 = wscale(w0lo, w0hi, kb);
       const float ws1 = MODE == M8_GATEUP ? wscale(w1lo, w1hi, kb) : ws0;
@@ -382,20 +385,25 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         fb[j] = join(B[bslot(j) * 128 + lane], B[bslot(j) * 128 + 64 + lane]);
-#pragma unroll
-      for (int m = 0; m < MH; ++m) {
+      f32x4_t p[2][4];
+      auto products = [&](int m) {
         const int mb = wr * MH + m;
         const i32x8_t fa = join(A[mb * 128 + lane], A[mb * 128 + 64 + lane]);
-        const f32x4_t sa = *(const f32x4_t*)(S + mb * 16 + 4 * q);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[m & 1][j] = mfma_fp8(fa, fb[j]);
+      };
+      products(0);
+#pragma unroll
+      for (int m = 0; m < MH; ++m) {
+        if (m + 1 < MH) products(m + 1);
+        const f32x4_t sa = *(const f32x4_t*)(S + (wr * MH + m) * 16 + 4 * q);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4_t p = mfma_fp8(fa, fb[j]);
           const float ws = (MODE == M8_GATEUP && j >= 2) ? ws1 : ws0;
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            acc[m][j][r] = __builtin_fmaf(p[r], sa[r] * ws, acc[m][j][r]);
+            acc[m][j][r] = __builtin_fmaf(p[m & 1][j][r], sa[r] * ws, acc[m][j][r]);
         }
-        if ((m & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound hoisting
       }
     };
     lds_barrier();                               // last item done with the ring
