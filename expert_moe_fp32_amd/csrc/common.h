@@ -35,28 +35,15 @@ __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-
 
 // ---------------------------------------------------------------- OCP E4M3
 // Round-to-nearest-even of a finite float32 to E4M3 ("e4m3fn": bias 7, no
-// infinities, S.1111.111 = NaN, max 448), saturating to +-448; sign copied.
+// infinities, S.1111.111 = NaN, max 448), saturating to +-448; sign copied
+// (also for results that round to zero).  gfx950's packed fp8 conversion
+// produces exactly these codes once the input is clamped to [-448, 448]
+// (the clamp is the saturation): it was compared bit for bit with a
+// bit-level software rounding of the definition on every float32 pattern
+// of magnitude below 1024, both signs, subnormals and zeros included.
 __device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x43E00000u) {                 // |v| >= 448
-    code = 0x7Eu;
-  } else if (a < 0x3C800000u) {           // |v| < 2^-6: subnormal range
-    // value = m * 2^-9 with m in [0, 8]; m = rne(|v| * 2^9)
-    float s = __uint_as_float(a) * 512.0f;  // exact scaling by a power of 2
-    uint32_t m = (uint32_t)__builtin_rintf(s);  // current rounding mode: RNE
-    code = m;                              // m == 8 is the smallest normal
-  } else {
-    // normal: keep 3 mantissa bits with RNE on the float32 bit pattern
-    uint32_t rounded = a + 0x7FFFFu + ((a >> 20) & 1u);
-    uint32_t e = (rounded >> 23) - 127 + 7;
-    uint32_t m = (rounded >> 20) & 7u;
-    code = (e << 3) | m;
-    if (code > 0x7Eu) code = 0x7Eu;
-  }
-  return (uint8_t)(sign | code);
+  const float c = __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFF);
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {

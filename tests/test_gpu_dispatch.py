@@ -109,3 +109,28 @@ def test_dispatch_edge_cases():
     assert d.phys_counts.tolist() == [0, 300, 0, 0]
     one = make_workload("tiny", seed=1, T=1)
     check_against_oracle(one, run_dispatch(one))
+
+
+def test_fp8_quantiser_every_bf16_value():
+    """Every finite bf16 value of magnitude <= 448, quantised with a unit
+    scale: each 128-channel group leads with +448 or -448, so amax / 448 = 1
+    and the codes are the E4M3 rounding of the values themselves.  Every
+    rounding boundary of E4M3 is a bf16 value, so this covers all of them,
+    the subnormal range, signed zero and the top of the range, bit for bit."""
+    pos = np.arange(0, 0x43E1, dtype=np.uint16)          # +0 .. +448
+    vals = np.concatenate([pos, pos | np.uint16(0x8000)])
+    H, per = 512, 127
+    groups = -(-len(vals) // per)
+    T = -(-groups // (H // 128))
+    g = np.zeros((T * (H // 128), 128), dtype=np.uint16)
+    g[:, 0] = 0x43E0                                      # +448
+    g[1::2, 0] = 0xC3E0                                   # -448
+    flat = np.zeros(g.shape[0] * per, dtype=np.uint16)
+    flat[: len(vals)] = vals
+    g[:, 1:] = flat.reshape(-1, per)
+    wl = make_workload("fp8", seed=3, T=T, H=H, I=128, E=8, num_local=8, k=2)
+    wl._cache["x"] = g.reshape(T, H)
+    print(f"quantiser: {len(vals)} bf16 values in {T} rows", flush=True)
+    got = run_dispatch(wl)
+    check_against_oracle(wl, got)
+    assert np.all(got["x_scales"] == 1.0)
