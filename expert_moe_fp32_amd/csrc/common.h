@@ -75,6 +75,14 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
 }
 
+// Non-temporal 16-byte load through the global address space.  Through a
+// generic pointer the load becomes a FLAT access, which may read LDS, so the
+// compiler waits for every outstanding LDS DMA before it.
+__device__ __forceinline__ u32x4_t load_global_nt(const u32x4_t* p) {
+  return __builtin_nontemporal_load(
+      (const __attribute__((address_space(1))) u32x4_t*)p);
+}
+
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 left at maximum).
 #define WAIT_VMCNT(n) \

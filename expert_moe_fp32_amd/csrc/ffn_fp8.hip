@@ -238,8 +238,8 @@ __global__ __launch_bounds__(256) void k_tile_fp8(K8Args a) {
 }
 
 // ------------------------------------------------------ LDS-ring kernel
-// For groups of up to 16 * NMB rows (one tile per expert at prefill-like
-// batches of ~130 rows per expert, a few rows at decode).  A workgroup of 8
+// For groups of up to 16 * NMB = 160 rows (one tile per expert at
+// prefill-like batches of ~130 rows per expert).  A workgroup of 8
 // wavefronts owns one tile and a group of output channels; each wavefront
 // owns two 16-channel weight columns -- gate and up of the same channels
 // (128 channels an item), or two down columns 128 channels apart (256 an
@@ -452,6 +452,217 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
   }
 }
 
+// ------------------------------------------------- weight-streaming kernel
+// For groups of a few rows (decode-sized tiles of up to 16 * NMB = 32 rows).  A workgroup of 8
+// wavefronts owns one tile and a group of output channels; each wavefront
+// owns two 16-channel weight columns -- gate and up of the same channels
+// (128 channels an item), or two down columns 128 channels apart (256 an
+// item) -- and all the tile's row blocks, so each weight byte is read once
+// per tile, the tile's activation rows once per 128 (256) channels, and the
+// SiLU epilogue needs no exchange.  The reduction runs in 128-wide K blocks
+// (one scale block each).  Each wavefront streams its two weight columns
+// straight into MFMA operand registers with non-temporal loads, three blocks
+// ahead (four register sets), so about 96 KiB of weights per CU are in
+// flight without LDS; the activation blocks (NMB of 2 KiB, lane order) and
+// the tile rows' scales, which all wavefronts share, go through a ring of 4
+// LDS stages that global_load_lds fills three blocks ahead.  Every
+// wavefront issues the same number of loads per block (A_PER activation
+// half-blocks -- ids past 2 * NMB repeat the last one, writing identical
+// bytes -- one 64-row scale slice, wavefronts past the last slice loading
+// 256 contiguous bytes into a dump slot, and four weight loads), so "this
+// block has landed" is one fixed vmcnt.  The weight scales of the two
+// columns sit one per lane (K <= 16384) and are read with readlane, so the
+// loop issues no other load.
+template <int MODE, int NMB>
+__global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
+  constexpr int NAB = 2 * NMB;                   // activation half-blocks
+  constexpr int A_PER = (NAB + 7) / 8;
+  constexpr int NRS = (16 * NMB + 63) / 64;      // 64-row scale slices
+  constexpr int C = A_PER + 1 + 4;               // loads per block per wave
+  __shared__ u32x4_t la0[NMB * 128], la1[NMB * 128], la2[NMB * 128], la3[NMB * 128];
+  __shared__ __attribute__((aligned(16))) float ls0[(NRS + 1) * 64],
+      ls1[(NRS + 1) * 64], ls2[(NRS + 1) * 64], ls3[(NRS + 1) * 64];  // slice NRS: dump
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, q = lane >> 4;
+  const int K = a.K, KB = K / 128;
+  const int total = a.tile_count[0] * a.nb_per_tile;
+  const int G = gridDim.x, per_xcd = G >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  for (int base = 0; base < total; base += G) {
+    const int item = base + xcd * per_xcd + slot;
+    if (item >= total) continue;                 // uniform for the workgroup
+    const int tile = item / a.nb_per_tile;
+    const int nb = item - tile * a.nb_per_tile;
+    const int4 td = a.tiles[tile];
+    const int g = td.x, row0 = td.y, nrows = td.z;
+    const bool sh = g == a.P;
+    const int nmb = (nrows + 15) >> 4;
+    const uint8_t* abase = sh ? a.a_shared : a.a_routed;
+    const float* sbase = sh ? a.as_shared : a.as_routed;
+    auto src_row = [&](int r) -> int {           // tile row -> source row
+      if (r >= nrows) r = 0;                     // padded rows read row 0
+      const int rr = row0 + r;
+      return sh ? rr : (a.a_rows ? a.a_rows[rr] : rr);
+    };
+    // activation half-blocks of this wavefront (id = 2 mb + half): with two
+    // or more per wavefront, both halves of row block wv come first, back to
+    // back, so the second finds the rows' cache lines in L1; the rest are
+    // dealt round-robin (ids past the last repeat it)
+    int arow[A_PER], aid[A_PER];
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      const int id = A_PER >= 2 ? (i < 2 ? 2 * wv + i : 16 + 8 * (i - 2) + wv)
+                                : wv;
+      aid[i] = min(id, NAB - 1);
+      arow[i] = src_row((aid[i] >> 1) * 16 + (lane & 15));
+    }
+    const int aoff = 32 * (lane >> 4);
+    // scale slice (rows 64 wv + lane) or the dump slot
+    const bool sreal = wv < NRS;
+    const int srow = src_row(64 * (sreal ? wv : 0) + lane);
+    // the two weight columns of this wavefront and their scale blocks (one
+    // 128-channel block per column)
+    int cb0, cb1;
+    const void *W0, *W1;
+    const float *sc0, *sc1;
+    if (MODE == M8_GATEUP) {
+      cb0 = cb1 = nb * 8 + wv;
+      W0 = sh ? a.w0_sh : a.w0_arr[g];
+      W1 = sh ? a.w1_sh : a.w1_arr[g];
+      sc0 = (sh ? a.s0_sh : a.s0_arr[g]) + (size_t)nb * KB;
+      sc1 = (sh ? a.s1_sh : a.s1_arr[g]) + (size_t)nb * KB;
+    } else {
+      cb0 = nb * 16 + wv;
+      cb1 = cb0 + 8;
+      W0 = W1 = sh ? a.w0_sh : a.w0_arr[g];
+      const float* S0 = sh ? a.s0_sh : a.s0_arr[g];
+      sc0 = S0 + (size_t)(2 * nb) * KB;
+      sc1 = S0 + (size_t)(2 * nb + 1) * KB;
+    }
+    const u32x4_t* wp0 = (const u32x4_t*)W0 + (size_t)cb0 * KB * 128 + lane;
+    const u32x4_t* wp1 = (const u32x4_t*)W1 + (size_t)cb1 * KB * 128 + lane;
+    // dump-slot source: 256 contiguous bytes of the column's own block
+    const float* sdump = (const float*)((const u32x4_t*)W0 + (size_t)cb0 * KB * 128) + lane;
+    const float w0lo = lane < KB ? sc0[lane] : 0.f;
+    const float w0hi = lane + 64 < KB ? sc0[lane + 64] : 0.f;
+    const float w1lo = lane < KB ? sc1[lane] : 0.f;
+    const float w1hi = lane + 64 < KB ? sc1[lane + 64] : 0.f;
+    auto wscale = [&](float lo, float hi, int kb) -> float {
+      const float v = kb < 64 ? lo : hi;
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kb & 63));
+    };
+
+    auto issue_a = [&](int kb, u32x4_t* A, float* S) {
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) {
+        const int id = aid[i];
+        lds_dma16(abase + (size_t)arow[i] * K + kb * 128 + aoff + 16 * (id & 1),
+                  A + (id >> 1) * 128 + (id & 1) * 64);
+      }
+      const float* sg = sreal ? sbase + (size_t)srow * KB + kb
+                              : sdump + (size_t)kb * 512;
+      __builtin_amdgcn_global_load_lds(sg, (lds_void*)(S + 64 * (sreal ? wv : NRS)),
+                                       4, 0, 0);
+    };
+    // weight operand of one K block: lane l holds bytes 16 l and 1024 + 16 l
+    // of the column's 2 KiB block
+    auto load_b = [&](int kb, i32x8_t* B) {
+      B[0] = join(load_global_nt(wp0 + (size_t)kb * 128),
+                  load_global_nt(wp0 + (size_t)kb * 128 + 64));
+      B[1] = join(load_global_nt(wp1 + (size_t)kb * 128),
+                  load_global_nt(wp1 + (size_t)kb * 128 + 64));
+    };
+    f32x4_t acc[NMB][2];
+#pragma unroll
+    for (int m = 0; m < NMB; ++m)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // All NMB row blocks run, straight-line, whatever nrows is: the MFMAs
+    // are cheap next to the weight stream, and a branch per block would
+    // make every block wait out its own LDS latency.  Padded rows hold row
+    // 0's data and are never stored.  The products of consecutive row blocks
+    // alternate between two register sets and block m + 1's MFMAs issue
+    // before block m's scaling, so MFMAs and scaling overlap.
+    auto compute = [&](int kb, const u32x4_t* A, const float* S, const i32x8_t* B) {
+      const float ws0 = wscale(w0lo, w0hi, kb);
+      const float ws1 = wscale(w1lo, w1hi, kb);
+      f32x4_t p[2][2];
+      auto products = [&](int m) {
+        const i32x8_t fa = join(A[m * 128 + lane], A[m * 128 + 64 + lane]);
+        p[m & 1][0] = mfma_fp8(fa, B[0]);
+        p[m & 1][1] = mfma_fp8(fa, B[1]);
+      };
+      products(0);
+#pragma unroll
+      for (int m = 0; m < NMB; ++m) {
+        if (m + 1 < NMB) products(m + 1);
+        const f32x4_t sa = *(const f32x4_t*)(S + m * 16 + 4 * q);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[m][0][r] = __builtin_fmaf(p[m & 1][0][r], sa[r] * ws0, acc[m][0][r]);
+          acc[m][1][r] = __builtin_fmaf(p[m & 1][1][r], sa[r] * ws1, acc[m][1][r]);
+        }
+      }
+    };
+    i32x8_t b0[2], b1[2], b2[2], b3[2];
+    lds_barrier();                               // last item done with the ring
+    issue_a(0, la0, ls0);
+    load_b(0, b0);
+    issue_a(min(1, KB - 1), la1, ls1);
+    load_b(min(1, KB - 1), b1);
+    issue_a(min(2, KB - 1), la2, ls2);
+    load_b(min(2, KB - 1), b2);
+    // Four blocks per trip; past the end a step re-issues the last K block
+    // into a slot (and register set) that is never read and computes
+    // nothing, so exactly two later blocks (C loads each) are in flight at
+    // every wait.
+    for (int kb = 0; kb < KB; kb += 4) {
+#define RING_STEP(J, AC, SC, BC, AN, SN, BN)                    \
+      {                                                         \
+        const int k = kb + J;                                   \
+        WAIT_VMCNT(2 * C);                                      \
+        lds_barrier();                                          \
+        const int kn = k + 3 < KB ? k + 3 : KB - 1;             \
+        issue_a(kn, AN, SN);                                    \
+        load_b(kn, BN);                                         \
+        if (k < KB) compute(k, AC, SC, BC);                     \
+        __builtin_amdgcn_sched_barrier(0);                      \
+      }
+      RING_STEP(0, la0, ls0, b0, la3, ls3, b3)
+      RING_STEP(1, la1, ls1, b1, la0, ls0, b0)
+      RING_STEP(2, la2, ls2, b2, la1, ls1, b1)
+      RING_STEP(3, la3, ls3, b3, la2, ls2, b2)
+#undef RING_STEP
+    }
+    WAIT_VMCNT(0);                               // trailing re-reads landed
+    // Epilogue from a wave-uniform 64-bit base and 32-bit offsets; N goes
+    // through an opaque move so the offsets are formed here rather than
+    // hoisted out of the item loop (hoisted, they spilled).
+    int N;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(N) : "s"(a.N));
+    float* out = MODE == M8_GATEUP
+                     ? a.h_out + ((size_t)(sh ? a.cap : 0) + row0) * N + cb0 * 16
+                     : (sh ? a.y_shared : a.y_routed) + (size_t)row0 * N + cb0 * 16;
+#pragma unroll
+    for (int m = 0; m < NMB; ++m) {
+      if (m >= nmb) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = m * 16 + 4 * q + r;
+        if (lr >= nrows) continue;
+        const int off = lr * N + c16;
+        if (MODE == M8_GATEUP) {
+          out[off] = silu_f32(acc[m][0][r]) * acc[m][1][r];
+        } else {
+          out[off] = acc[m][0][r];
+          out[off + (cb1 - cb0) * 16] = acc[m][1][r];
+        }
+      }
+    }
+  }
+}
+
 // Quantise float32 h rows per 128 channels: routed rows [0, N) (N read on the
 // device) and shared rows [cap, cap + T_sh).  A lane takes 8 channels (two
 // 16-byte loads), the 16 lanes of a DPP row one 128-channel group.
@@ -522,11 +733,12 @@ hipError_t launch_pack_fp8(const uint8_t* src, int R, int C, void* dst,
   return hipGetLastError();
 }
 
-// Tile rows of the FP8 recipe for an expected group size: the LDS-ring
-// weight-streaming kernel with 32-row tiles (a few rows per expert) or
-// 160-row tiles (one tile per expert up to 160 rows), both balanced; else
-// the 128 x 128 tiled kernel.  The ring's down pass covers 256 channels an
-// item, so it needs H % 256 == 0.
+// Tile rows of the FP8 recipe for an expected group size: the
+// register weight-streaming kernel with 32-row tiles (a few rows per
+// expert) or the LDS-ring kernel with 160-row tiles (one tile per expert up
+// to 160 rows), both balanced; else the 128 x 128 tiled kernel.  Both
+// streaming kernels' down pass covers 256 channels an item, so they need
+// H % 256 == 0.
 int ffn_fp8_tile_rows(int rows_hint, int H, int I, int* balanced) {
   (void)I;
   *balanced = 0;
@@ -539,7 +751,7 @@ template <int MODE>
 static void launch_stream_fp8(const K8Args& a, int BM, hipStream_t s) {
   // one workgroup per CU (LDS); a multiple of 8 for the XCD-major order
   if (BM == 32)
-    k_ring_fp8<MODE, 2><<<256, 512, 0, s>>>(a);
+    k_wstream_fp8<MODE, 2><<<256, 512, 0, s>>>(a);
   else
     k_ring_fp8<MODE, 10><<<256, 512, 0, s>>>(a);
 }
