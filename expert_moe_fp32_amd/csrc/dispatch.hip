@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void k_permute(
 // the expert FFN's tile list: fewer dependent launches on the decode path.
 // Same positions as the multi-block path: the pair's rank inside its
 // 64-token wavefront comes from a ballot, earlier wavefronts from LDS.
-static constexpr int kSmallT = 1024, kSmallL = 256;
+static constexpr int kSmallT = 1024, kSmallL = 256, kSmallMap = 2048;
 
 bool dispatch_small_ok(int T, int E, int L, int P) {
   return T <= kSmallT && L <= kSmallL && E <= MOE_EMAX && P <= MOE_LMAX;
@@ -218,8 +218,18 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
   __shared__ int32_t tb[MOE_LMAX + 2];
   __shared__ int32_t wpre[16 * kSmallL];
   __shared__ uint64_t bal[16 * kSmallL];    // per wavefront: ballot per expert
+  __shared__ int32_t reps[kSmallL];         // replica counts (clamped)
+  __shared__ int32_t maps[kSmallMap];       // the replica map when it fits
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   const int T = a.T, k = a.k, L = a.num_local, P = a.P;
+  // The replica counts and map are loaded into LDS here, alongside the
+  // ids, rather than read from global memory where they are needed: two
+  // dependent round trips fewer on this single-workgroup path.
+  const bool map_lds = a.l2p && L * a.max_rep <= kSmallMap;
+  for (int i = t; i < L; i += 1024)
+    reps[i] = a.rep ? min(max(a.rep[i], 1), a.max_rep) : 1;
+  if (map_lds)
+    for (int i = t; i < L * a.max_rep; i += 1024) maps[i] = a.l2p[i];
   for (int i = t; i < x.E; i += 1024) cnt[i] = 0;
   for (int i = t; i <= P; i += 1024) pc[i] = 0;
   __syncthreads();
@@ -255,9 +265,9 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
       wpre[v * kSmallL + e] = run;
       run += c;
     }
-    const int R = a.rep ? min(max(a.rep[e], 1), a.max_rep) : 1;
+    const int R = reps[e];
     for (int r = 0; r < R; ++r) {
-      const int p = a.l2p ? a.l2p[e * a.max_rep + r] : e;
+      const int p = !a.l2p ? e : map_lds ? maps[e * a.max_rep + r] : a.l2p[e * a.max_rep + r];
       if (p >= 0 && p < P) pc[p] = run > r ? (run - r + R - 1) / R : 0;
     }
   }
@@ -324,8 +334,9 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
       continue;
     }
     const int n = wpre[wv * kSmallL + e] + __popcll(bal[wv * kSmallL + e] & lt);
-    const int R = a.rep ? min(max(a.rep[e], 1), a.max_rep) : 1;
-    const int p = a.l2p ? a.l2p[e * a.max_rep + (n % R)] : e;
+    const int R = reps[e];
+    const int mi = e * a.max_rep + (n % R);
+    const int p = !a.l2p ? e : map_lds ? maps[mi] : a.l2p[mi];
     if (p < 0 || p >= P) {
       a.pair_row[o] = -1;
       continue;
