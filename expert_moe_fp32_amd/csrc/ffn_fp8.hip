@@ -247,18 +247,20 @@ __global__ __launch_bounds__(256) void k_tile_fp8(K8Args a) {
 // rows are re-read once per 128 (256) channels, and the SiLU epilogue needs
 // no exchange.  Operands come through a ring of 3 LDS stages of one 128-wide
 // K block each (one scale block) that global_load_lds fills two stages ahead
-// without holding registers.  A stage holds the tile's activation blocks
-// (NMB of 2 KiB, lane order), the 16 weight blocks (2 KiB each) and the tile
-// rows' scales.  Every wavefront issues the same number of loads per stage
-// (A_PER activation half-blocks -- ids past 2 * NMB repeat the last one,
-// writing identical bytes -- four weight halves and one 64-row scale slice;
+// without holding registers.  A stage holds the tile's activation rows
+// (2 NMB blocks of 8 rows x 128 bytes, each moved whole by one transfer and
+// swizzled as described at the staging code), the 16 weight blocks (2 KiB
+// each, lane order) and the tile rows' scales.  Every wavefront issues the
+// same number of loads per stage (A_PER activation blocks -- ids past
+// 2 NMB repeat the last one, writing identical bytes -- four weight halves
+// and one 64-row scale slice;
 // wavefronts past the last slice load 256 contiguous bytes into a dump
 // slot), so "this stage has landed" is one fixed vmcnt.  The weight scales
 // of the two columns sit one per lane (K <= 16384) and are read with
 // readlane, so the loop issues no global load of its own.
 template <int MODE, int NMB>
 __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
-  constexpr int NAB = 2 * NMB;                   // activation half-blocks
+  constexpr int NAB = 2 * NMB;                   // 8-row activation blocks
   constexpr int A_PER = (NAB + 7) / 8;
   constexpr int NRS = (16 * NMB + 63) / 64;      // 64-row scale slices
   constexpr int C = A_PER + 4 + 1;               // loads per stage per wave
@@ -289,19 +291,24 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
       const int rr = row0 + r;
       return sh ? rr : (a.a_rows ? a.a_rows[rr] : rr);
     };
-    // activation half-blocks of this wavefront (id = 2 mb + half): with two
-    // or more per wavefront, both halves of row block wv come first, back to
-    // back, so the second finds the rows' cache lines in L1; the rest are
-    // dealt round-robin (ids past the last repeat it)
-    int arow[A_PER], aid[A_PER];
+    // Activation staging: one transfer moves the whole 128-byte K block of
+    // 8 rows (8-row block b = id, dealt round-robin, ids past the last
+    // repeating it): lane i loads row 8 b + (i >> 3), 16-byte chunk
+    // (i & 7) ^ (i >> 3) ^ (b & 1), landing in slot i & 7 of that row.
+    int arow[A_PER], achunk[A_PER], aid[A_PER];
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-      const int id = A_PER >= 2 ? (i < 2 ? 2 * wv + i : 16 + 8 * (i - 2) + wv)
-                                : wv;
-      aid[i] = min(id, NAB - 1);
-      arow[i] = src_row((aid[i] >> 1) * 16 + (lane & 15));
+      aid[i] = min(wv + 8 * i, NAB - 1);
+      arow[i] = src_row(aid[i] * 8 + (lane >> 3));
+      achunk[i] = 16 * ((lane & 7) ^ (lane >> 3) ^ (aid[i] & 1));
     }
-    const int aoff = 32 * (lane >> 4);
+    // MFMA operand of row block mb: lane l takes row l % 16 (8-row block
+    // 2 mb + (l % 16) / 8), chunks 2 (l / 16) and 2 (l / 16) + 1, found at
+    // slot chunk ^ (row % 8) ^ (block parity); the 16 lanes of a read hit 16
+    // different bank groups.
+    const int ab = (lane >> 3) & 1, ar = lane & 7;
+    const int a_lo = ab * 64 + ar * 8 + ((2 * (lane >> 4)) ^ ar ^ ab);
+    const int a_hi = ab * 64 + ar * 8 + ((2 * (lane >> 4) + 1) ^ ar ^ ab);
     // scale slice (rows 64 wv + lane) or the dump slot
     const bool sreal = wv < NRS;
     const int srow = src_row(64 * (sreal ? wv : 0) + lane);
@@ -347,9 +354,8 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
     auto issue = [&](int kb, u32x4_t* A, u32x4_t* B, float* S) {
 #pragma unroll
       for (int i = 0; i < A_PER; ++i) {
-        const int id = aid[i];
-        lds_dma16(abase + (size_t)arow[i] * K + kb * 128 + aoff + 16 * (id & 1),
-                  A + (id >> 1) * 128 + (id & 1) * 64);
+        lds_dma16(abase + (size_t)arow[i] * K + kb * 128 + achunk[i],
+                  A + aid[i] * 64);
       }
       lds_dma16(wp0 + (size_t)kb * 128, B + wv * 128);
       lds_dma16(wp0 + (size_t)kb * 128 + 64, B + wv * 128 + 64);
@@ -388,7 +394,7 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
       f32x4_t p[2][4];
       auto products = [&](int m) {
         const int mb = wr * MH + m;
-        const i32x8_t fa = join(A[mb * 128 + lane], A[mb * 128 + 64 + lane]);
+        const i32x8_t fa = join(A[mb * 128 + a_lo], A[mb * 128 + a_hi]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) p[m & 1][j] = mfma_fp8(fa, fb[j]);
       };
@@ -428,6 +434,14 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
 #undef RING_STEP
     }
     WAIT_VMCNT(0);                               // trailing re-reads landed
+    // Epilogue from a wave-uniform 64-bit base and 32-bit offsets; N goes
+    // through an opaque move so the offsets are formed here rather than
+    // hoisted out of the item loop (hoisted, they held registers).
+    int N;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(N) : "s"(a.N));
+    float* out = MODE == M8_GATEUP
+                     ? a.h_out + ((size_t)(sh ? a.cap : 0) + row0) * N + (nb * 8 + 2 * wc) * 16
+                     : (sh ? a.y_shared : a.y_routed) + (size_t)row0 * N + (nb * 16 + 4 * wc) * 16;
 #pragma unroll
     for (int m = 0; m < MH; ++m) {
       const int mb = wr * MH + m;
@@ -436,16 +450,14 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
       for (int r = 0; r < 4; ++r) {
         const int lr = mb * 16 + 4 * q + r;
         if (lr >= nrows) continue;
+        const int off = lr * N + c16;
         if (MODE == M8_GATEUP) {
-          const size_t hr = (size_t)(sh ? a.cap : 0) + row0 + lr;
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            a.h_out[hr * a.N + (nb * 8 + 2 * wc + j) * 16 + c16] =
-                silu_f32(acc[m][j][r]) * acc[m][2 + j][r];
+            out[off + j * 16] = silu_f32(acc[m][j][r]) * acc[m][2 + j][r];
         } else {
-          float* y = (sh ? a.y_shared : a.y_routed) + (size_t)(row0 + lr) * a.N;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) y[(nb * 16 + 4 * wc + j) * 16 + c16] = acc[m][j][r];
+          for (int j = 0; j < 4; ++j) out[off + j * 16] = acc[m][j][r];
         }
       }
     }
@@ -463,19 +475,19 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
 // (one scale block each).  Each wavefront streams its two weight columns
 // straight into MFMA operand registers with non-temporal loads, three blocks
 // ahead (four register sets), so about 96 KiB of weights per CU are in
-// flight without LDS; the activation blocks (NMB of 2 KiB, lane order) and
-// the tile rows' scales, which all wavefronts share, go through a ring of 4
-// LDS stages that global_load_lds fills three blocks ahead.  Every
-// wavefront issues the same number of loads per block (A_PER activation
-// half-blocks -- ids past 2 * NMB repeat the last one, writing identical
-// bytes -- one 64-row scale slice, wavefronts past the last slice loading
+// flight without LDS; the activation rows (2 NMB blocks of 8 rows x 128
+// bytes, staged as in k_ring_fp8) and the tile rows' scales, which all
+// wavefronts share, go through a ring of 4 LDS stages that global_load_lds
+// fills three blocks ahead.  Every wavefront issues the same number of
+// loads per block (A_PER activation blocks -- ids past 2 NMB repeat the
+// last one, writing identical bytes -- one 64-row scale slice, wavefronts past the last slice loading
 // 256 contiguous bytes into a dump slot, and four weight loads), so "this
 // block has landed" is one fixed vmcnt.  The weight scales of the two
 // columns sit one per lane (K <= 16384) and are read with readlane, so the
 // loop issues no other load.
 template <int MODE, int NMB>
 __global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
-  constexpr int NAB = 2 * NMB;                   // activation half-blocks
+  constexpr int NAB = 2 * NMB;                   // 8-row activation blocks
   constexpr int A_PER = (NAB + 7) / 8;
   constexpr int NRS = (16 * NMB + 63) / 64;      // 64-row scale slices
   constexpr int C = A_PER + 1 + 4;               // loads per block per wave
@@ -505,19 +517,24 @@ __global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
       const int rr = row0 + r;
       return sh ? rr : (a.a_rows ? a.a_rows[rr] : rr);
     };
-    // activation half-blocks of this wavefront (id = 2 mb + half): with two
-    // or more per wavefront, both halves of row block wv come first, back to
-    // back, so the second finds the rows' cache lines in L1; the rest are
-    // dealt round-robin (ids past the last repeat it)
-    int arow[A_PER], aid[A_PER];
+    // Activation staging: one transfer moves the whole 128-byte K block of
+    // 8 rows (8-row block b = id, dealt round-robin, ids past the last
+    // repeating it): lane i loads row 8 b + (i >> 3), 16-byte chunk
+    // (i & 7) ^ (i >> 3) ^ (b & 1), landing in slot i & 7 of that row.
+    int arow[A_PER], achunk[A_PER], aid[A_PER];
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-      const int id = A_PER >= 2 ? (i < 2 ? 2 * wv + i : 16 + 8 * (i - 2) + wv)
-                                : wv;
-      aid[i] = min(id, NAB - 1);
-      arow[i] = src_row((aid[i] >> 1) * 16 + (lane & 15));
+      aid[i] = min(wv + 8 * i, NAB - 1);
+      arow[i] = src_row(aid[i] * 8 + (lane >> 3));
+      achunk[i] = 16 * ((lane & 7) ^ (lane >> 3) ^ (aid[i] & 1));
     }
-    const int aoff = 32 * (lane >> 4);
+    // MFMA operand of row block mb: lane l takes row l % 16 (8-row block
+    // 2 mb + (l % 16) / 8), chunks 2 (l / 16) and 2 (l / 16) + 1, found at
+    // slot chunk ^ (row % 8) ^ (block parity); the 16 lanes of a read hit 16
+    // different bank groups.
+    const int ab = (lane >> 3) & 1, ar = lane & 7;
+    const int a_lo = ab * 64 + ar * 8 + ((2 * (lane >> 4)) ^ ar ^ ab);
+    const int a_hi = ab * 64 + ar * 8 + ((2 * (lane >> 4) + 1) ^ ar ^ ab);
     // scale slice (rows 64 wv + lane) or the dump slot
     const bool sreal = wv < NRS;
     const int srow = src_row(64 * (sreal ? wv : 0) + lane);
@@ -556,9 +573,8 @@ __global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
     auto issue_a = [&](int kb, u32x4_t* A, float* S) {
 #pragma unroll
       for (int i = 0; i < A_PER; ++i) {
-        const int id = aid[i];
-        lds_dma16(abase + (size_t)arow[i] * K + kb * 128 + aoff + 16 * (id & 1),
-                  A + (id >> 1) * 128 + (id & 1) * 64);
+        lds_dma16(abase + (size_t)arow[i] * K + kb * 128 + achunk[i],
+                  A + aid[i] * 64);
       }
       const float* sg = sreal ? sbase + (size_t)srow * KB + kb
                               : sdump + (size_t)kb * 512;
@@ -589,7 +605,7 @@ __global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
       const float ws1 = wscale(w1lo, w1hi, kb);
       f32x4_t p[2][2];
       auto products = [&](int m) {
-        const i32x8_t fa = join(A[m * 128 + lane], A[m * 128 + 64 + lane]);
+        const i32x8_t fa = join(A[m * 128 + a_lo], A[m * 128 + a_hi]);
         p[m & 1][0] = mfma_fp8(fa, B[0]);
         p[m & 1][1] = mfma_fp8(fa, B[1]);
       };
