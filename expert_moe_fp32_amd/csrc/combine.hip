@@ -1,19 +1,28 @@
 // Combine: un-permute and sum each token's expert outputs weighted by its
 // route weights ("6.4 Data parallelism and expert parallelism", section 3.1,
 // step 4), plus the shared expert's output with weight 1 (section 2.1).
-// Workgroup (token t, 1024-column chunk); each thread owns 4 columns and
-// issues the loads of all the token's local rows before it accumulates, in
-// float32 and slot order, with one rounding to the output type.
+// Workgroup = (token, column slice); a slice is the whole row unless the
+// batch is too small to fill the GPU.  The first wavefront compacts the
+// token's local slots (slot order kept) into LDS while every thread already
+// loads its columns of the shared expert's row; then each thread owns
+// groups of 4 columns, CPT groups per pass, and issues all of a pass's row
+// loads before it accumulates, in float32 and slot order, with one rounding
+// to the output type.
 #include "common.h"
 
 namespace moe {
+
+static constexpr int kCombineCPT = 4;      // column groups per thread per pass
 
 template <int OUT_BF16>
 __global__ __launch_bounds__(256) void k_combine(
     const float* __restrict__ y, const int32_t* __restrict__ pair_row,
     const float* __restrict__ w, const float* __restrict__ y_shared, int T,
-    int H, int k, void* __restrict__ out) {
+    int H, int k, int cw, void* __restrict__ out) {
+  constexpr int CPT = kCombineCPT;
   const int t = blockIdx.x;
+  const int H4 = H >> 2;
+  const int cbeg = blockIdx.y * cw, cend = min(H4, cbeg + cw);
   __shared__ int32_t rows[MOE_KMAX];
   __shared__ float wts[MOE_KMAX];
   __shared__ int nloc;
@@ -29,41 +38,61 @@ __global__ __launch_bounds__(256) void k_combine(
     }
     if (j == 0) nloc = __popcll(m);
   }
+  // the first pass's shared-expert columns do not depend on the slots
+  const float* ys = y_shared ? y_shared + (size_t)t * H : nullptr;
+  f32x4_t sh0[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = cbeg + threadIdx.x + 256 * i;
+    sh0[i] = (ys && c < cend) ? *(const f32x4_t*)(ys + 4 * c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   __syncthreads();
   const int n = nloc;
-  const int H4 = H >> 2;
-  const int c = blockIdx.y * blockDim.x + threadIdx.x;
-  if (c < H4) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < n; j0 += 4) {      // four rows' loads in flight
-      f32x4_t v[4];
+  for (int c0 = cbeg + threadIdx.x; c0 < cend; c0 += 256 * CPT) {
+    f32x4_t acc[CPT];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {          // past n: re-read the last row
-        const int j = min(j0 + q, n - 1);
-        v[q] = *(const f32x4_t*)(y + (size_t)rows[j] * H + 4 * c);
+    for (int i = 0; i < CPT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t shv[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = c0 + 256 * i;
+      shv[i] = c0 == cbeg + (int)threadIdx.x ? sh0[i]
+               : (ys && c < cend) ? *(const f32x4_t*)(ys + 4 * c)
+                                : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int j = 0; j < n; ++j) {
+      const float* yr = y + (size_t)rows[j] * H;
+      const float wj = wts[j];
+      f32x4_t v[CPT];
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = c0 + 256 * i;
+        v[i] = c < cend ? *(const f32x4_t*)(yr + 4 * c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (j0 + q < n) {
-          const float wj = wts[j0 + q];
-          acc.x = __builtin_fmaf(wj, v[q].x, acc.x);
-          acc.y = __builtin_fmaf(wj, v[q].y, acc.y);
-          acc.z = __builtin_fmaf(wj, v[q].z, acc.z);
-          acc.w = __builtin_fmaf(wj, v[q].w, acc.w);
-        }
+      for (int i = 0; i < CPT; ++i) {
+        acc[i].x = __builtin_fmaf(wj, v[i].x, acc[i].x);
+        acc[i].y = __builtin_fmaf(wj, v[i].y, acc[i].y);
+        acc[i].z = __builtin_fmaf(wj, v[i].z, acc[i].z);
+        acc[i].w = __builtin_fmaf(wj, v[i].w, acc[i].w);
       }
     }
-    if (y_shared) {
-      const f32x4_t v = *(const f32x4_t*)(y_shared + (size_t)t * H + 4 * c);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    if (OUT_BF16) {
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
-      pk.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
-      *(uint2*)((bf16_t*)out + (size_t)t * H + 4 * c) = pk;
-    } else {
-      *(f32x4_t*)((float*)out + (size_t)t * H + 4 * c) = acc;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = c0 + 256 * i;
+      if (c >= cend) continue;
+      f32x4_t s = acc[i];
+      if (ys) {
+        s.x += shv[i].x; s.y += shv[i].y; s.z += shv[i].z; s.w += shv[i].w;
+      }
+      if (OUT_BF16) {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
+        pk.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
+        *(uint2*)((bf16_t*)out + (size_t)t * H + 4 * c) = pk;
+      } else {
+        *(f32x4_t*)((float*)out + (size_t)t * H + 4 * c) = s;
+      }
     }
   }
 }
@@ -72,11 +101,17 @@ hipError_t launch_combine(const float* y_perm, const int32_t* pair_row,
                           const float* w, const float* y_shared, int T, int H,
                           int k, int out_dtype, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const dim3 grid(T, (H / 4 + 255) / 256);
+  // column slices (multiples of 256 groups of 4) so that small batches
+  // still launch about 2048 workgroups
+  const int H4 = H / 4;
+  const int groups = (H4 + 255) / 256;
+  const int want = T >= 2048 ? 1 : min(groups, (2048 + T - 1) / T);
+  const int cw = ((groups + want - 1) / want) * 256;
+  const dim3 grid(T, (H4 + cw - 1) / cw);
   if (out_dtype == MOE_BF16)
-    k_combine<1><<<grid, 256, 0, s>>>(y_perm, pair_row, w, y_shared, T, H, k, out);
+    k_combine<1><<<grid, 256, 0, s>>>(y_perm, pair_row, w, y_shared, T, H, k, cw, out);
   else
-    k_combine<0><<<grid, 256, 0, s>>>(y_perm, pair_row, w, y_shared, T, H, k, out);
+    k_combine<0><<<grid, 256, 0, s>>>(y_perm, pair_row, w, y_shared, T, H, k, cw, out);
   return hipGetLastError();
 }
 
