@@ -56,20 +56,20 @@ TRAFFIC = {
         kernel="k_stream_bf16<0, 2>",
         files=("expert_moe_fp32_amd/csrc/ffn.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="04e6a8e1e7ebc214", fetch_kib=794479.3, write_kib=988.3,
+        sha="43914d07d21521c4", fetch_kib=794479.4, write_kib=988.3,
         fetch_factor=1.9969, write_factor=1.0),
     "prefill": dict(
         kernel="k_gemm_bf16<0, 4, 2, 2, 4>",
         files=("expert_moe_fp32_amd/csrc/gemm_bf16.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="9231f8118f172206", fetch_kib=2386616.0, write_kib=88744.2,
+        sha="d4578fceeec6c312", fetch_kib=2347712.9, write_kib=65704.0,
         fetch_factor=1.9973, write_factor=1.0),
     "fp8": dict(
         kernel="k_ring_fp8<0, 10>",
         files=("expert_moe_fp32_amd/csrc/ffn_fp8.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="879a9b856507e02d", fetch_kib=473973.2, write_kib=33232.0,
-        fetch_factor=1.9956, write_factor=1.0),
+        sha="19953807fb1cc870", fetch_kib=474012.5, write_kib=33232.0,
+        fetch_factor=1.9965, write_factor=1.0),
 }
 
 
