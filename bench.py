@@ -194,8 +194,8 @@ def main():
                     help="oracle sample size (0 = workload default)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; "
-                          "--gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark measures one EP rank's "
+                          "share on one GPU; --gpus must be 1"}))
         sys.exit(2)
 
     import torch
