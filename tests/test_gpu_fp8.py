@@ -76,8 +76,13 @@ def run_fp8_layer(wl):
     # LDS-ring weight streaming, 160-row tiles (one per expert), ragged;
     # gate/up runs two trips of its 4-stage loop
     dict(T=200, H=1024, I=512, E=16, num_local=8, k=4),
-    # LDS-ring weight streaming, 32-row tiles (a few rows per expert)
+    # register weight streaming (k_wstream_fp8), 32-row tiles (a few rows
+    # per expert)
     dict(T=64, H=512, I=512, E=32, num_local=8, k=4),
+    # the same kernel with 6 K blocks in gate/up (the last trip of its
+    # 4-block loop half past the end) and 2 in down (the prologue clamps
+    # its third block to the last one)
+    dict(T=64, H=768, I=256, E=32, num_local=8, k=4),
     # LDS-ring streaming with the shared expert's 300 rows in 160-row tiles
     dict(T=300, H=512, I=512, E=8, num_local=8, k=2, shared=True),
     # 128 x 128 tiled kernel (H not a multiple of 256; many rows per
