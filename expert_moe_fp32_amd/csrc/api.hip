@@ -85,11 +85,6 @@ FfnScratch carve_ffn(Carver& c, const moe_problem* p) {
   return f;
 }
 
-// recipes whose expert kernels exist
-bool ffn_built(const moe_problem* p) {
-  return p != nullptr;
-}
-
 // Expected rows per physical expert: the local pairs over the physical
 // experts, where a rank with fewer physical than logical experts (a
 // group-wide placement whose other replicas sit on other ranks) expects
@@ -387,7 +382,6 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm,
   moe_status st = moe_check_problem(p);
   if (st != MOE_OK) return st;
   if ((st = check_weights(p, w)) != MOE_OK) return st;
-  if (!ffn_built(p)) return MOE_ERR_UNSUPPORTED;
   if (p->T == 0) return MOE_OK;
   if (!x_perm || !offsets || !y_perm) return MOE_ERR_INVALID_ARGUMENT;
   const bool fp8 = p->weight_dtype == MOE_FP8_E4M3;
@@ -427,7 +421,6 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
   if (st != MOE_OK) return st;
   if ((st = check_map(p, l2p, replica_count)) != MOE_OK) return st;
   if ((st = check_weights(p, w)) != MOE_OK) return st;
-  if (!ffn_built(p)) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = S(stream);
   if (p->T == 0) {
     if (expert_counts)
