@@ -490,7 +490,8 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   } else if (stream) {
     a.nb_per_tile = a.N / 64;
     long items = max_tiles * a.nb_per_tile;
-    long grid = items < cu * 16 ? items : cu * 16;
+    // persistent: the two workgroups a CU holds at this kernel's registers
+    long grid = items < cu * 2 ? items : cu * 2;
     k_stream_bf16<MODE_GATEUP, 2><<<(unsigned)grid, 256, 0, s>>>(a);
   } else {                                  // ring: bf16 beyond streaming
     hipError_t e = launch_gemm_bf16_gateup(f, s);
@@ -520,7 +521,8 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   } else if (stream) {
     a.nb_per_tile = a.N / 128;                // two 64-apart blocks per wave
     long items = max_tiles * a.nb_per_tile;
-    long grid = items < cu * 16 ? items : cu * 16;
+    // persistent: the two workgroups a CU holds at this kernel's registers
+    long grid = items < cu * 2 ? items : cu * 2;
     k_stream_bf16<MODE_DOWN, 2><<<(unsigned)grid, 256, 0, s>>>(a);
   } else if (ring && f.H % 256 == 0) {
     hipError_t e = launch_gemm_bf16_down(f, s);
