@@ -56,7 +56,7 @@ TRAFFIC = {
         kernel="k_stream_bf16<0, 2>",
         files=("expert_moe_fp32_amd/csrc/ffn.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="43914d07d21521c4", fetch_kib=794479.4, write_kib=988.3,
+        sha="2fee451fd5e7b304", fetch_kib=794481.0, write_kib=988.8,
         fetch_factor=1.9969, write_factor=1.0),
     "prefill": dict(
         kernel="k_gemm_bf16<0, 4, 2, 2, 4>",
