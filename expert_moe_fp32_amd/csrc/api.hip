@@ -156,7 +156,7 @@ moe_status dispatch_impl(const moe_problem* p, const void* x,
                          int32_t* pair_row, const DispatchScratch& d,
                          hipStream_t s, hipEvent_t ev_index = nullptr,
                          bool materialize = true,
-                         const SmallExtras* extras = nullptr) {
+                         const DispatchExtras* extras = nullptr) {
   DispatchArgs a{};
   a.T = p->T;
   a.k = p->k;
@@ -176,14 +176,13 @@ moe_status dispatch_impl(const moe_problem* p, const void* x,
   a.row_weight = row_weight;
   a.pair_row = pair_row;
   hipError_t e;
-  if (dispatch_small_ok(p->T, p->E, p->num_local, p->num_physical)) {
-    SmallExtras x{};
-    x.E = p->E;
-    if (extras) x = *extras;
-    e = launch_dispatch_small(a, x, s);
-  } else {
-    e = launch_dispatch_index(a, s);
-  }
+  DispatchExtras xt{};
+  xt.E = p->E;
+  if (extras) xt = *extras;
+  if (dispatch_small_ok(p->T, p->E, p->num_local, p->num_physical))
+    e = launch_dispatch_small(a, xt, s);
+  else
+    e = launch_dispatch_index(a, xt, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (ev_index) hipEventRecord(ev_index, s);
   const int cap = (int)cap_rows(p);
@@ -436,19 +435,18 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
   LayerScratch L = carve_layer(c, p);
   if (ev) hipEventRecord(ev[0], s);
   int32_t* counts = expert_counts ? expert_counts : L.counts;
-  // Small batches: the single-workgroup dispatch also counts the experts
-  // and writes the FFN tile list, so neither needs a launch of its own.
+  // The dispatch's single-workgroup stage writes the FFN tile list, so it
+  // needs no launch of its own; for small batches it also counts the
+  // experts.
   const bool small = dispatch_small_ok(p->T, p->E, p->num_local, p->num_physical);
-  SmallExtras extras{};
+  DispatchExtras extras{};
   extras.E = p->E;
-  if (small) {
-    extras.counts = counts;
-    extras.tiles = L.f.tiles;
-    extras.tile_count = L.f.tile_count;
-    extras.BM = ffn_tile_rows(p->act_dtype, p->weight_dtype, rows_hint(p),
-                              p->H, p->I, &extras.balanced);
-    extras.has_shared = p->has_shared;
-  }
+  if (small) extras.counts = counts;
+  extras.tiles = L.f.tiles;
+  extras.tile_count = L.f.tile_count;
+  extras.BM = ffn_tile_rows(p->act_dtype, p->weight_dtype, rows_hint(p),
+                            p->H, p->I, &extras.balanced);
+  extras.has_shared = p->has_shared;
   // the router's count pass stores every entry of counts (no zero fill)
   if (launch_route_topk(logits, bias, p->T, p->E, p->k, L.ids, L.tw,
                         small ? nullptr : counts, s) != hipSuccess)
@@ -457,7 +455,7 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
   st = dispatch_impl(p, x, L.ids, L.tw, l2p, replica_count, L.x_perm,
                      L.x_perm_scales, L.offsets, L.row_token, L.row_weight,
                      L.pair_row, L.d, s, ev ? ev[2] : nullptr,
-                     /*materialize=*/false, small ? &extras : nullptr);
+                     /*materialize=*/false, &extras);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[3], s);
   // The expert kernels read each routed row straight from the token rows
@@ -469,7 +467,7 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
                          p->has_shared ? xs : nullptr,
                          p->has_shared && fp8 ? L.d.xs : nullptr, w, L.y_perm,
                          L.y_shared, L.f, s, ev ? ev + 4 : nullptr,
-                         L.row_token, /*tiles_ready=*/small);
+                         L.row_token, /*tiles_ready=*/true);
   if (st != MOE_OK) return st;
   st = hip_status(launch_combine(L.y_perm, L.pair_row, L.tw,
                                  p->has_shared ? L.y_shared : nullptr, p->T,

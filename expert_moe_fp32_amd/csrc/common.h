@@ -126,11 +126,11 @@ struct DispatchArgs {
   int32_t* pair_row;
 };
 int dispatch_blocks(int T);
-hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s);
 
-// single-workgroup variant for small batches; optionally also writes the
-// expert counts over all E and the expert FFN's tile list
-struct SmallExtras {
+// Optional outputs of the dispatch's single-workgroup stage (the whole
+// small-batch kernel, or the multi-block path's scan): the expert FFN's tile
+// list and, small-batch kernel only, the expert counts over all E.
+struct DispatchExtras {
   int E;
   int32_t* counts;        // [E] or null
   int4* tiles;            // or null
@@ -139,7 +139,10 @@ struct SmallExtras {
   int balanced;           // near-equal tiles (multiples of 16 rows)
 };
 bool dispatch_small_ok(int T, int E, int L, int P);
-hipError_t launch_dispatch_small(const DispatchArgs& a, const SmallExtras& x,
+hipError_t launch_dispatch_small(const DispatchArgs& a, const DispatchExtras& x,
+                                 hipStream_t s);
+// multi-block dispatch index; x.tiles (optional) receives the FFN tile list
+hipError_t launch_dispatch_index(const DispatchArgs& a, const DispatchExtras& x,
                                  hipStream_t s);
 
 // x_perm[r] = x[row_token[r]] for r < offsets[P]; row_bytes % 16 == 0

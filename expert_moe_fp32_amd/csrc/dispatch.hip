@@ -111,12 +111,54 @@ __global__ __launch_bounds__(256) void k_local_hist(
         wave_cnt[e] + wave_cnt[L + e] + wave_cnt[2 * L + e] + wave_cnt[3 * L + e];
 }
 
+// FFN tile list from the segment offsets held in LDS (off[0 .. P]) by a
+// single workgroup: wavefront 0 counts each group's tiles and scans them
+// into tb (G + 1 entries, G = P + shared), the workgroup barrier follows,
+// then every thread writes its groups' tiles.  Called by all threads.
+__device__ void tile_list_from_offsets(const int32_t* off, int P, int T,
+                                       const DispatchExtras& x, int32_t* tb) {
+  const int G = P + (x.has_shared ? 1 : 0);
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int nt_carry = 0;
+    for (int base = 0; base < G; base += 64) {
+      const int g = base + lane;
+      int nt = 0;
+      if (g < G) {
+        const int rows = g < P ? off[g + 1] - off[g] : T;
+        int per;
+        nt = tile_split(rows, x.BM, x.balanced, &per);
+      }
+      int tot;
+      const int ex = wave_excl_scan(nt, &tot);
+      if (g < G) tb[g] = nt_carry + ex;
+      nt_carry += tot;
+    }
+    if (lane == 0) {
+      tb[G] = nt_carry;
+      x.tile_count[0] = nt_carry;
+    }
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    const int start = g < P ? off[g] : 0;
+    const int rows = g < P ? off[g + 1] - start : T;
+    if (rows == 0) continue;
+    int per;
+    tile_split(rows, x.BM, x.balanced, &per);
+    int i = tb[g];
+    for (int r = 0; r < rows; r += per, ++i)
+      x.tiles[i] = make_int4(g, start + r, min(per, rows - r), 0);
+  }
+}
+
 __global__ __launch_bounds__(1024) void k_scan(
     const int32_t* __restrict__ block_counts, int nblk, int L, int P,
     int max_rep, const int32_t* __restrict__ l2p,
     const int32_t* __restrict__ rep, int32_t* __restrict__ block_base,
-    int32_t* __restrict__ offsets) {
-  __shared__ int32_t pc[MOE_LMAX];
+    int32_t* __restrict__ offsets, int T, DispatchExtras x) {
+  __shared__ int32_t pc[MOE_LMAX + 1];
+  __shared__ int32_t tb[MOE_LMAX + 2];
   for (int p = threadIdx.x; p < P; p += blockDim.x) pc[p] = 0;
   __syncthreads();
   for (int e = threadIdx.x; e < L; e += blockDim.x) {
@@ -146,9 +188,16 @@ __global__ __launch_bounds__(1024) void k_scan(
       const int p = base + lane;
       int tot;
       const int ex = wave_excl_scan(p < P ? pc[p] : 0, &tot);
-      if (p <= P) offsets[p] = carry + ex;
+      if (p <= P) {
+        offsets[p] = carry + ex;
+        pc[p] = carry + ex;                // offsets stay in LDS for the tiles
+      }
       carry += tot;
     }
+  }
+  if (x.tiles) {                           // uniform
+    __syncthreads();
+    tile_list_from_offsets(pc, P, T, x, tb);
   }
 }
 
@@ -207,12 +256,13 @@ __global__ __launch_bounds__(256) void k_permute(
 // 64-token wavefront comes from a ballot, earlier wavefronts from LDS.
 static constexpr int kSmallT = 1024, kSmallL = 256, kSmallMap = 2048;
 
+
 bool dispatch_small_ok(int T, int E, int L, int P) {
   return T <= kSmallT && L <= kSmallL && E <= MOE_EMAX && P <= MOE_LMAX;
 }
 
 __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
-                                                         SmallExtras x) {
+                                                         DispatchExtras x) {
   __shared__ int32_t cnt[MOE_EMAX];
   __shared__ int32_t pc[MOE_LMAX + 1];
   __shared__ int32_t tb[MOE_LMAX + 2];
@@ -287,42 +337,9 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
       }
       carry += tot;
     }
-    if (x.tiles) {                         // tile list of the expert FFN
-      const int G = P + (x.has_shared ? 1 : 0);
-      int nt_carry = 0;
-      for (int base = 0; base < G; base += 64) {
-        const int g = base + lane;
-        int nt = 0;
-        if (g < G) {
-          const int rows = g < P ? pc[g + 1] - pc[g] : T;
-          int per;
-          nt = tile_split(rows, x.BM, x.balanced, &per);
-        }
-        int tot;
-        const int ex = wave_excl_scan(nt, &tot);
-        if (g < G) tb[g] = nt_carry + ex;
-        nt_carry += tot;
-      }
-      if (lane == 0) {
-        tb[G] = nt_carry;
-        x.tile_count[0] = nt_carry;
-      }
-    }
   }
   __syncthreads();
-  if (x.tiles) {
-    const int G = P + (x.has_shared ? 1 : 0);
-    for (int g = t; g < G; g += 1024) {
-      const int start = g < P ? pc[g] : 0;
-      const int rows = g < P ? pc[g + 1] - start : T;
-      if (rows == 0) continue;
-      int per;
-      tile_split(rows, x.BM, x.balanced, &per);
-      int i = tb[g];
-      for (int r = 0; r < rows; r += per, ++i)
-        x.tiles[i] = make_int4(g, start + r, min(per, rows - r), 0);
-    }
-  }
+  if (x.tiles) tile_list_from_offsets(pc, P, T, x, tb);   // uniform
   if (t >= T) return;
 #pragma unroll
   for (int j = 0; j < MOE_KMAX; ++j) {
@@ -348,19 +365,21 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
   }
 }
 
-hipError_t launch_dispatch_small(const DispatchArgs& a, const SmallExtras& x,
+hipError_t launch_dispatch_small(const DispatchArgs& a, const DispatchExtras& x,
                                  hipStream_t s) {
   k_dispatch_small<<<1, 1024, 0, s>>>(a, x);
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s) {
+hipError_t launch_dispatch_index(const DispatchArgs& a, const DispatchExtras& x,
+                                 hipStream_t s) {
   const int nblk = dispatch_blocks(a.T);
   const size_t lds = sizeof(int32_t) * 4 * a.num_local;
   k_local_hist<<<nblk, 256, lds, s>>>(a.ids, a.T, a.k, a.expert_begin,
                                       a.num_local, a.block_counts);
   k_scan<<<1, 1024, 0, s>>>(a.block_counts, nblk, a.num_local, a.P,
-                            a.max_rep, a.l2p, a.rep, a.block_base, a.offsets);
+                            a.max_rep, a.l2p, a.rep, a.block_base, a.offsets,
+                            a.T, x);
   const size_t lds_perm = (sizeof(uint64_t) + sizeof(int32_t)) * 4 * a.num_local;
   k_permute<<<nblk, 256, lds_perm, s>>>(a.ids, a.w, a.T, a.k, a.expert_begin,
                                    a.num_local, a.P, a.max_rep, a.l2p, a.rep,

@@ -448,14 +448,16 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   const int BM = ffn_tile_rows(f.act, f.wdt, f.rows_hint, f.H, f.I, &balanced);
   const bool stream = !f32 && BM == 32;
   const bool ring = !f32 && balanced;     // tiles of up to 256 rows
-  // the ring GEMM's list (or the only list), plus down's 128-row list; a
-  // list already written by the dispatch is the first one
+  // the ring GEMM's list (or the only list), plus down's 128-row list when
+  // down runs the 128 x 128 tile kernel (H not a multiple of 256); a list
+  // already written by the dispatch is the first one
+  const bool down_list = ring && f.H % 256 != 0;
   if (!f.tiles_ready)
     k_build_tiles<<<1, 1024, 0, s>>>(f.offsets, f.P, f.has_shared, f.T, BM,
                                      balanced, f.tiles, f.tile_count, TBM,
-                                     ring ? f.tiles_down : nullptr,
+                                     down_list ? f.tiles_down : nullptr,
                                      f.tile_count + 1);
-  else if (ring)
+  else if (down_list)
     k_build_tiles<<<1, 1024, 0, s>>>(f.offsets, f.P, f.has_shared, f.T, TBM, 0,
                                      f.tiles_down, f.tile_count + 1, TBM,
                                      nullptr, nullptr);
