@@ -63,6 +63,10 @@ def sample_tokens(T, n, seed=0):
     ("decode", dict(T=700, H=256, I=384, E=8, num_local=8, k=2)),    # tiled
     # ring GEMM gate/up, 128 x 128 tiled down (H not a multiple of 256)
     ("prefill", dict(T=400, H=384, I=256, E=8, num_local=8, k=2)),
+    # more than 1024 tokens: the multi-block dispatch, whose scan writes the
+    # tile list (ring GEMM + 128-row down list; fp32 kernel)
+    ("prefill", dict(T=1100, H=384, I=256, E=8, num_local=8, k=2)),
+    ("tiny", dict(T=1500, E=16, num_local=8, k=2)),
 ])
 def test_layer_reduced_shapes(name, kw):
     wl = make_workload(name, seed=11, **kw)
