@@ -40,6 +40,7 @@ inline moe_status hip_status(hipError_t e) {
 struct DispatchScratch {
   int32_t* block_counts;
   int32_t* block_base;
+  int32_t* block_ecounts;  // [nblk][E] partial expert counts
   uint8_t* xq;     // fp8: [T][H] codes of every token
   float* xs;       // fp8: [T][H/128]
 };
@@ -49,6 +50,7 @@ DispatchScratch carve_dispatch(Carver& c, const moe_problem* p) {
   const size_t nb = (size_t)dispatch_blocks(p->T) * p->num_local;
   d.block_counts = c.take<int32_t>(nb);
   d.block_base = c.take<int32_t>(nb);
+  d.block_ecounts = c.take<int32_t>((size_t)dispatch_blocks(p->T) * p->E);
   if (p->weight_dtype == MOE_FP8_E4M3) {
     d.xq = c.take<uint8_t>((size_t)p->T * p->H);
     d.xs = c.take<float>((size_t)p->T * (p->H / 128));
@@ -171,6 +173,7 @@ moe_status dispatch_impl(const moe_problem* p, const void* x,
   a.rep = rep;
   a.block_counts = d.block_counts;
   a.block_base = d.block_base;
+  a.block_ecounts = d.block_ecounts;
   a.offsets = offsets;
   a.row_token = row_token;
   a.row_weight = row_weight;
@@ -435,21 +438,18 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
   LayerScratch L = carve_layer(c, p);
   if (ev) hipEventRecord(ev[0], s);
   int32_t* counts = expert_counts ? expert_counts : L.counts;
-  // The dispatch's single-workgroup stage writes the FFN tile list, so it
-  // needs no launch of its own; for small batches it also counts the
-  // experts.
-  const bool small = dispatch_small_ok(p->T, p->E, p->num_local, p->num_physical);
+  // The dispatch's single-workgroup stage counts the experts and writes the
+  // FFN tile list, so neither needs a launch of its own.
   DispatchExtras extras{};
   extras.E = p->E;
-  if (small) extras.counts = counts;
+  extras.counts = counts;
   extras.tiles = L.f.tiles;
   extras.tile_count = L.f.tile_count;
   extras.BM = ffn_tile_rows(p->act_dtype, p->weight_dtype, rows_hint(p),
                             p->H, p->I, &extras.balanced);
   extras.has_shared = p->has_shared;
-  // the router's count pass stores every entry of counts (no zero fill)
   if (launch_route_topk(logits, bias, p->T, p->E, p->k, L.ids, L.tw,
-                        small ? nullptr : counts, s) != hipSuccess)
+                        nullptr, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (ev) hipEventRecord(ev[1], s);
   st = dispatch_impl(p, x, L.ids, L.tw, l2p, replica_count, L.x_perm,

@@ -120,6 +120,7 @@ struct DispatchArgs {
   const int32_t* rep;       // may be null
   int32_t* block_counts;    // [nblk][L]
   int32_t* block_base;      // [nblk][L]
+  int32_t* block_ecounts;   // [nblk][E] partial expert counts (multi-block)
   int32_t* offsets;         // [P+1]
   int32_t* row_token;
   float* row_weight;
@@ -129,7 +130,7 @@ int dispatch_blocks(int T);
 
 // Optional outputs of the dispatch's single-workgroup stage (the whole
 // small-batch kernel, or the multi-block path's scan): the expert FFN's tile
-// list and, small-batch kernel only, the expert counts over all E.
+// list and the expert counts over all E.
 struct DispatchExtras {
   int E;
   int32_t* counts;        // [E] or null

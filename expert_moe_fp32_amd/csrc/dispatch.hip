@@ -94,12 +94,23 @@ __device__ __forceinline__ void for_each_expert_ballot(
   }
 }
 
+// Per block of tokens: the rows of each local expert, and (block_ecounts
+// non-null) the block's pairs of every one of the E experts, counted in an
+// LDS histogram and stored for the scan to sum.
 __global__ __launch_bounds__(256) void k_local_hist(
     const int32_t* __restrict__ ids, int T, int k, int e0, int L,
-    int32_t* __restrict__ block_counts) {
-  extern __shared__ int32_t wave_cnt[];     // [4][L]
+    int32_t* __restrict__ block_counts, int E,
+    int32_t* __restrict__ block_ecounts) {
+  extern __shared__ int32_t wave_cnt[];     // [4][L], then [E]
+  int32_t* ehist = wave_cnt + 4 * L;
   const int t = blockIdx.x * kTokPerBlock + threadIdx.x;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (block_ecounts) {                      // uniform
+    for (int e = threadIdx.x; e < E; e += blockDim.x) ehist[e] = 0;
+    __syncthreads();
+    if (t < T)
+      for (int j = 0; j < k; ++j) atomicAdd(&ehist[ids[(size_t)t * k + j]], 1);
+  }
   int le[MOE_KMAX];
   load_local_ids(ids, t, T, k, e0, L, le);
   for_each_expert_ballot(le, L, [&](int e, uint64_t m) {
@@ -109,6 +120,9 @@ __global__ __launch_bounds__(256) void k_local_hist(
   for (int e = threadIdx.x; e < L; e += blockDim.x)
     block_counts[(size_t)blockIdx.x * L + e] =
         wave_cnt[e] + wave_cnt[L + e] + wave_cnt[2 * L + e] + wave_cnt[3 * L + e];
+  if (block_ecounts)
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      block_ecounts[(size_t)blockIdx.x * E + e] = ehist[e];
 }
 
 // FFN tile list from the segment offsets held in LDS (off[0 .. P]) by a
@@ -156,9 +170,24 @@ __global__ __launch_bounds__(1024) void k_scan(
     const int32_t* __restrict__ block_counts, int nblk, int L, int P,
     int max_rep, const int32_t* __restrict__ l2p,
     const int32_t* __restrict__ rep, int32_t* __restrict__ block_base,
-    int32_t* __restrict__ offsets, int T, DispatchExtras x) {
+    int32_t* __restrict__ offsets, int T, DispatchExtras x,
+    const int32_t* __restrict__ block_ecounts) {
   __shared__ int32_t pc[MOE_LMAX + 1];
   __shared__ int32_t tb[MOE_LMAX + 2];
+  if (x.counts) {                          // expert counts: sum the block rows
+    for (int e = threadIdx.x; e < x.E; e += blockDim.x) {
+      int c = 0;
+      for (int b0 = 0; b0 < nblk; b0 += 8) {   // eight loads in flight
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = b0 + u < nblk ? block_ecounts[(size_t)(b0 + u) * x.E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c += v[u];
+      }
+      x.counts[e] = c;
+    }
+  }
   for (int p = threadIdx.x; p < P; p += blockDim.x) pc[p] = 0;
   __syncthreads();
   for (int e = threadIdx.x; e < L; e += blockDim.x) {
@@ -374,12 +403,13 @@ hipError_t launch_dispatch_small(const DispatchArgs& a, const DispatchExtras& x,
 hipError_t launch_dispatch_index(const DispatchArgs& a, const DispatchExtras& x,
                                  hipStream_t s) {
   const int nblk = dispatch_blocks(a.T);
-  const size_t lds = sizeof(int32_t) * 4 * a.num_local;
+  int32_t* ecounts = x.counts ? a.block_ecounts : nullptr;
+  const size_t lds = sizeof(int32_t) * (4 * a.num_local + (ecounts ? x.E : 0));
   k_local_hist<<<nblk, 256, lds, s>>>(a.ids, a.T, a.k, a.expert_begin,
-                                      a.num_local, a.block_counts);
+                                      a.num_local, a.block_counts, x.E, ecounts);
   k_scan<<<1, 1024, 0, s>>>(a.block_counts, nblk, a.num_local, a.P,
                             a.max_rep, a.l2p, a.rep, a.block_base, a.offsets,
-                            a.T, x);
+                            a.T, x, ecounts);
   const size_t lds_perm = (sizeof(uint64_t) + sizeof(int32_t)) * 4 * a.num_local;
   k_permute<<<nblk, 256, lds_perm, s>>>(a.ids, a.w, a.T, a.k, a.expert_begin,
                                    a.num_local, a.P, a.max_rep, a.l2p, a.rep,
