@@ -56,19 +56,19 @@ TRAFFIC = {
         kernel="k_stream_bf16<0, 2>",
         files=("expert_moe_fp32_amd/csrc/ffn.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="2fee451fd5e7b304", fetch_kib=794481.0, write_kib=988.8,
+        sha="3d950f29938a63d4", fetch_kib=794521.5, write_kib=988.7,
         fetch_factor=1.9969, write_factor=1.0),
     "prefill": dict(
         kernel="k_gemm_bf16<0, 4, 2, 2, 4>",
         files=("expert_moe_fp32_amd/csrc/gemm_bf16.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="d4578fceeec6c312", fetch_kib=2347712.9, write_kib=65704.0,
+        sha="de797d2a746d81a3", fetch_kib=2350902.7, write_kib=65704.0,
         fetch_factor=1.9973, write_factor=1.0),
     "fp8": dict(
         kernel="k_ring_fp8<0, 10>",
         files=("expert_moe_fp32_amd/csrc/ffn_fp8.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="19953807fb1cc870", fetch_kib=474012.5, write_kib=33232.0,
+        sha="2f8e3c32d0afb25d", fetch_kib=474075.2, write_kib=33232.0,
         fetch_factor=1.9965, write_factor=1.0),
 }
 
