@@ -817,6 +817,7 @@ hipError_t launch_ffn_fp8(FfnArgs& f, hipStream_t s) {
     k_tile_fp8<M8_GATEUP><<<(unsigned)grid, 256, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (f.events) hipEventRecord(f.events[1], s);   // gate/up kernel alone
   // ---- h -> E4M3 per row per 128 channels
   {
     long qg = (hrows * (f.I / 8) + 255) / 256;
@@ -828,7 +829,6 @@ hipError_t launch_ffn_fp8(FfnArgs& f, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (f.events) hipEventRecord(f.events[1], s);
   // ---- down
   a.K = f.I;
   a.N = f.H;

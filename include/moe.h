@@ -227,7 +227,8 @@ MOE_API moe_status moe_layer_forward(const moe_problem* p, const float* logits,
  * handles created by the caller; recorded in order
  *   [0] start  [1] route done  [2] dispatch index done  [3] row gather done
  *   [4] FFN tile list built  [5] gate/up done  [6] down done  [7] combine done
- * (on the T = 0 path nothing is recorded). */
+ * (on the T = 0 path nothing is recorded).  In the FP8 recipe the
+ * quantisation of h to E4M3 falls in the down interval [5, 6]. */
 #define MOE_STAGE_EVENTS 8
 MOE_API moe_status moe_layer_forward_timed(const moe_problem* p,
                                    const float* logits, const float* bias,
