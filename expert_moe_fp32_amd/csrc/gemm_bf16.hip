@@ -10,10 +10,11 @@
 // global_load_lds_dwordx4 (each lane's 16 bytes land at the transfer's base
 // + 16 * lane, so no registers stage the copy): B in a ring of 4 stages of 16
 // column blocks of 1 KiB, A in 2 slots of a stage pair, where one transfer
-// moves 8 whole 128-byte row segments (64 K) -- a transfer of 16 rows x 64
-// bytes, half a cache line per row, ran the loop about 14 % slower.  Every
-// fragment read is one conflict-free ds_read_b128; one barrier per stage,
-// loads two to three stages ahead of the MFMAs.
+// moves 8 whole 128-byte row segments (64 K), each read by 8 consecutive
+// lanes, so every group of 8 lanes touches one cache line (lanes spread over
+// 8 lines per group ran gate/up 6 % slower, 16 rows x 64 bytes slower
+// still).  Every fragment read is one conflict-free ds_read_b128; one
+// barrier per stage, loads two to three stages ahead of the MFMAs.
 //
 // Placement: workgroups are dealt round-robin to the 8 XCDs (workgroup b on
 // XCD b % 8).  Items are numbered column block fastest, so consecutive items
@@ -94,21 +95,22 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
     const bool sh = g == a.P;
     // This wavefront stages A blocks w + NW h (8 rows of a stage pair) and
     // B column blocks w + NW h.  An A transfer takes 128 contiguous bytes
-    // (64 K) of each of 8 rows: lane i loads row 8b + (i & 7), stage i >> 5
-    // of the pair, 8-element chunk c = ((i >> 3) & 3) ^ (b & 1), and lands
-    // at 16 i, so a block holds the pair's first stage in its first 512
-    // bytes and its second in the rest, each as [chunk slot][row].
+    // (64 K, 8 chunks of 8 elements: chunks 0-3 the pair's first stage,
+    // 4-7 its second) of each of 8 rows: lane i loads row 8b + i / 8, chunk
+    // (i % 8) ^ z with z = 4 (b & 1) + i / 16 (the row's index inside its
+    // 32-row block, halved, mod 8), and lands at 16 i, so a block is
+    // [row][chunk slot].
     const bf16_t* ga[HA];
     const u32x4_t* gb[HB];
 #pragma unroll
     for (int h = 0; h < HA; ++h) {
       const int b8 = w + NW * h;
-      int r = b8 * 8 + (lane & 7);
+      int r = b8 * 8 + (lane >> 3);
       if (r >= nrows) r = 0;               // padded rows read row 0, unused
       const int rr = row0 + r;
       const bf16_t* rowp = sh ? a.a_shared + (size_t)rr * K
                               : a.a_routed + (size_t)(a.a_rows ? a.a_rows[rr] : rr) * K;
-      ga[h] = rowp + (lane >> 5) * 32 + ((((lane >> 3) & 3) ^ (b8 & 1)) * 8);
+      ga[h] = rowp + (((lane & 7) ^ ((b8 & 1) * 4 + (lane >> 4))) * 8);
     }
 #pragma unroll
     for (int h = 0; h < HB; ++h) {
@@ -138,16 +140,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
     const int valid_rows = nrows - wm * TM * 32;   // may be <= 0
-    // stage HH of the pair in slot A: lane l reads row l % 32 of a 32-row
-    // block (8-row block (l % 32) / 8, its row l % 8), chunk 2 s + l / 32 at
-    // chunk slot chunk ^ ((l >> 3) & 1); the 16 lanes of a read cover two
-    // 128-byte runs in opposite bank halves
+    // stage HH of the pair in slot A: lane l reads row r = l % 32 of a
+    // 32-row block (8-row block r / 8, its row r % 8), chunk
+    // c = 4 HH + 2 s + l / 32 at chunk slot c ^ ((r / 2) % 8); the 16 lanes
+    // of a read take 16 distinct 16-byte bank groups (row parity x slot)
     auto compute = [&](const u32x4_t* A, int HH, const u32x4_t* B) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int pos = c16 + 16 * (2 * s + ks);   // lane slot inside a B block
-        const int apos = ((lane & 31) >> 3) * 64 + HH * 32 + (lane & 7) +
-                         8 * ((2 * s + ks) ^ ((lane >> 3) & 1));
+        const int apos = ((lane & 31) >> 3) * 64 + (lane & 7) * 8 +
+                         ((HH * 4 + 2 * s + ks) ^ (((lane & 31) >> 1) & 7));
         u32x4_t fb[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
