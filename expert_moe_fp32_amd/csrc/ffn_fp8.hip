@@ -351,6 +351,22 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
       return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kb & 63));
     };
 
+    // transfer i of stage kb, in the order issue() uses: A blocks, the four
+    // weight blocks, the row scales
+    auto dma = [&](int i, int kb, u32x4_t* A, u32x4_t* B, float* S) {
+      if (i < A_PER) {
+        lds_dma16(abase + (size_t)arow[i] * K + kb * 128 + achunk[i], A + aid[i] * 64);
+      } else if (i < A_PER + 4) {
+        const int b = i - A_PER;
+        const u32x4_t* wp = b < 2 ? wp0 : wp1;
+        lds_dma16(wp + (size_t)kb * 128 + 64 * (b & 1), B + ((b < 2 ? 0 : 8) + wv) * 128 + 64 * (b & 1));
+      } else {
+        const float* sg = sreal ? sbase + (size_t)srow * KB + kb
+                                : sdump + (size_t)kb * 512;
+        __builtin_amdgcn_global_load_lds(sg, (lds_void*)(S + 64 * (sreal ? wv : NRS)),
+                                         4, 0, 0);
+      }
+    };
     auto issue = [&](int kb, u32x4_t* A, u32x4_t* B, float* S) {
 #pragma unroll
       for (int i = 0; i < A_PER; ++i) {
@@ -384,7 +400,9 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
     // alternate between two register sets and block m + 1's MFMAs issue
     // before block m's scaling: with one temporary, each MFMA waited for the
     // previous product's scaling and each scaling for its MFMA's result.
-    auto compute = [&](int kb, const u32x4_t* A, const u32x4_t* B, const float* S) {
+    constexpr int NT = A_PER + 5;                // transfers per stage
+    auto compute = [&](int kb, const u32x4_t* A, const u32x4_t* B, const float* S,
+                       auto&& xfer) {
       const float ws0 = wscale(w0lo, w0hi, kb);
       const float ws1 = MODE == M8_GATEUP ? wscale(w1lo, w1hi, kb) : ws0;
       i32x8_t fb[4];
@@ -402,6 +420,9 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
 #pragma unroll
       for (int m = 0; m < MH; ++m) {
         if (m + 1 < MH) products(m + 1);
+        // the next stage's transfers, spread over the row blocks' MFMAs
+#pragma unroll
+        for (int i = m * NT / MH; i < (m + 1) * NT / MH; ++i) xfer(i);
         const f32x4_t sa = *(const f32x4_t*)(S + (wr * MH + m) * 16 + 4 * q);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -417,22 +438,34 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
     issue(min(1, KB - 1), la1, lb1, ls1);
     // Three stages per trip; past the end a step re-issues the last K block
     // into a slot that is never read and computes nothing, so exactly one
-    // later stage (C loads) is in flight at every wait.
-    for (int kb = 0; kb < KB; kb += 3) {
-#define RING_STEP(J, AC, BC, SC, AN, BN, SN)                    \
+    // later stage (C loads) is in flight at every wait.  A step's transfers
+    // of the stage two ahead go out between its row blocks' MFMAs rather
+    // than all at once after the barrier, where the wavefronts' 64 transfers
+    // queued at the address unit and stalled their issue (gate/up -5 %).
+    // Full trips run without conditions; the last partial trip computes only
+    // its real stages.
+    int kb = 0;
+#define RING_STEP(J, AC, BC, SC, AN, BN, SN, TAIL)              \
       {                                                         \
         const int k = kb + J;                                   \
+        const int kn = k + 2 < KB ? k + 2 : KB - 1;             \
         WAIT_VMCNT(C);                                          \
         lds_barrier();                                          \
-        issue(k + 2 < KB ? k + 2 : KB - 1, AN, BN, SN);         \
-        if (k < KB) compute(k, AC, BC, SC);                     \
+        auto xf = [&](int i) { dma(i, kn, AN, BN, SN); };       \
+        if (!TAIL || k < KB) compute(k, AC, BC, SC, xf);        \
+        else issue(kn, AN, BN, SN);                             \
         __builtin_amdgcn_sched_barrier(0);                      \
       }
-      RING_STEP(0, la0, lb0, ls0, la2, lb2, ls2)
-      RING_STEP(1, la1, lb1, ls1, la0, lb0, ls0)
-      RING_STEP(2, la2, lb2, ls2, la1, lb1, ls1)
-#undef RING_STEP
+    for (; kb + 3 <= KB; kb += 3) {
+      RING_STEP(0, la0, lb0, ls0, la2, lb2, ls2, false)
+      RING_STEP(1, la1, lb1, ls1, la0, lb0, ls0, false)
+      RING_STEP(2, la2, lb2, ls2, la1, lb1, ls1, false)
     }
+    if (kb < KB) {
+      RING_STEP(0, la0, lb0, ls0, la2, lb2, ls2, true)
+      RING_STEP(1, la1, lb1, ls1, la0, lb0, ls0, true)
+    }
+#undef RING_STEP
     WAIT_VMCNT(0);                               // trailing re-reads landed
     // Epilogue from a wave-uniform 64-bit base and 32-bit offsets; N goes
     // through an opaque move so the offsets are formed here rather than
