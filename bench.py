@@ -68,7 +68,7 @@ TRAFFIC = {
         kernel="k_ring_fp8<0, 10>",
         files=("expert_moe_fp32_amd/csrc/ffn_fp8.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="03e7f122194f30da", fetch_kib=474212.4, write_kib=33232.1,
+        sha="78bf07f721b517aa", fetch_kib=474342.9, write_kib=33232.0,
         fetch_factor=1.9965, write_factor=1.0),
 }
 

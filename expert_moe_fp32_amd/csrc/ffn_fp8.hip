@@ -273,7 +273,14 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
   const int c16 = lane & 15, q = lane >> 4;
   const int K = a.K, KB = K / 128;
   const int total = a.tile_count[0] * a.nb_per_tile;
-  const int G = gridDim.x, per_xcd = G >> 3;
+  // As many workgroups as make the rounds of the persistent loop equal (a
+  // multiple of 8 for the XCD mapping); the rest exit at once.  A short last
+  // round leaves the weight stream to a fraction of the CUs (low-latency
+  // layer -2 %).
+  const int rounds = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int G = min((int)gridDim.x, (((total + rounds - 1) / max(rounds, 1)) + 7) & ~7);
+  const int per_xcd = G >> 3;
+  if ((int)blockIdx.x >= G) return;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   for (int base = 0; base < total; base += G) {
     const int item = base + xcd * per_xcd + slot;
@@ -532,7 +539,14 @@ __global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
   const int c16 = lane & 15, q = lane >> 4;
   const int K = a.K, KB = K / 128;
   const int total = a.tile_count[0] * a.nb_per_tile;
-  const int G = gridDim.x, per_xcd = G >> 3;
+  // As many workgroups as make the rounds of the persistent loop equal (a
+  // multiple of 8 for the XCD mapping); the rest exit at once.  A short last
+  // round leaves the weight stream to a fraction of the CUs (low-latency
+  // layer -2 %).
+  const int rounds = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int G = min((int)gridDim.x, (((total + rounds - 1) / max(rounds, 1)) + 7) & ~7);
+  const int per_xcd = G >> 3;
+  if ((int)blockIdx.x >= G) return;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   for (int base = 0; base < total; base += G) {
     const int item = base + xcd * per_xcd + slot;
