@@ -83,6 +83,9 @@ def run_fp8_layer(wl):
     # 4-block loop half past the end) and 2 in down (the prologue clamps
     # its third block to the last one)
     dict(T=64, H=768, I=256, E=32, num_local=8, k=4),
+    # the ring with K-block counts that are multiples of its 3-stage trip
+    # (6 in gate/up, 3 in down: no partial last trip)
+    dict(T=200, H=768, I=384, E=16, num_local=8, k=4),
     # LDS-ring streaming with the shared expert's 300 rows in 160-row tiles
     dict(T=300, H=512, I=512, E=8, num_local=8, k=2, shared=True),
     # 128 x 128 tiled kernel (H not a multiple of 256; many rows per
