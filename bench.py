@@ -68,7 +68,7 @@ TRAFFIC = {
         kernel="k_ring_fp8<0, 10>",
         files=("expert_moe_fp32_amd/csrc/ffn_fp8.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="78bf07f721b517aa", fetch_kib=474342.9, write_kib=33232.0,
+        sha="743f037bac8df097", fetch_kib=474023.7, write_kib=33232.0,
         fetch_factor=1.9965, write_factor=1.0),
 }
 

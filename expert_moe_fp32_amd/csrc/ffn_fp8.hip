@@ -358,20 +358,24 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
       return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kb & 63));
     };
 
-    // transfer i of stage kb, in the order issue() uses: A blocks, the four
-    // weight blocks, the row scales
+    // transfer i of stage kb: the row scales first (a 4-byte gather over 64
+    // rows, the slowest transfer for the address unit: first, it overlaps
+    // the most; gate/up -4 %), then the A blocks, then the four weight
+    // blocks.  Only whole stages are waited for, so the order inside one is
+    // free.
     auto dma = [&](int i, int kb, u32x4_t* A, u32x4_t* B, float* S) {
-      if (i < A_PER) {
-        lds_dma16(abase + (size_t)arow[i] * K + kb * 128 + achunk[i], A + aid[i] * 64);
-      } else if (i < A_PER + 4) {
-        const int b = i - A_PER;
-        const u32x4_t* wp = b < 2 ? wp0 : wp1;
-        lds_dma16(wp + (size_t)kb * 128 + 64 * (b & 1), B + ((b < 2 ? 0 : 8) + wv) * 128 + 64 * (b & 1));
-      } else {
+      if (i == 0) {
         const float* sg = sreal ? sbase + (size_t)srow * KB + kb
                                 : sdump + (size_t)kb * 512;
         __builtin_amdgcn_global_load_lds(sg, (lds_void*)(S + 64 * (sreal ? wv : NRS)),
                                          4, 0, 0);
+      } else if (i <= A_PER) {
+        lds_dma16(abase + (size_t)arow[i - 1] * K + kb * 128 + achunk[i - 1],
+                  A + aid[i - 1] * 64);
+      } else {
+        const int b = i - 1 - A_PER;
+        const u32x4_t* wp = b < 2 ? wp0 : wp1;
+        lds_dma16(wp + (size_t)kb * 128 + 64 * (b & 1), B + ((b < 2 ? 0 : 8) + wv) * 128 + 64 * (b & 1));
       }
     };
     auto issue = [&](int kb, u32x4_t* A, u32x4_t* B, float* S) {
