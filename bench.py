@@ -62,7 +62,7 @@ TRAFFIC = {
         kernel="k_gemm_bf16<0, 4, 2, 2, 4>",
         files=("expert_moe_fp32_amd/csrc/gemm_bf16.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="6be74bac576b0b73", fetch_kib=1890216.9, write_kib=65704.0,
+        sha="04112b138a402e5f", fetch_kib=1890216.9, write_kib=65704.0,
         fetch_factor=1.9973, write_factor=1.0),
     "fp8": dict(
         kernel="k_ring_fp8<0, 10>",

@@ -61,17 +61,6 @@ __device__ __forceinline__ f32x16_t mfma32b(u32x4_t a, u32x4_t b, f32x16_t c) {
                                                  c, 0, 0, 0);
 }
 
-// Workgroup = WM x WN wavefronts; wavefront (wm, wn) owns TM x TN blocks of
-// 32 x 32 computed with v_mfma_f32_32x32x16_bf16 (on gfx950 this instruction
-// sustains about 1.6x the rate of the 16x16x32 form), so a tile is
-// 32*TM*WM rows x 32*TN*WN B-columns.  B stages hold the tile's 16-column x
-// 32-K blocks (1 KiB, lane order): a 16 x 32 B operand is read from two
-// adjacent blocks, lane l taking column l % 32 (block (l % 32) / 16, its
-// column l % 16) and K-slot 2s + l / 32 of the stage (substep s = 0, 1), so
-// 16 lanes read 256 contiguous bytes.  A pair slots hold 8-row blocks laid
-// out as described at the staging code; lane l reads row l % 32 and the same
-// K-slot.  The accumulator of lane l holds column l % 32 and rows
-// 8 * (r / 4) + 4 * (l / 32) + r % 4, r < 16.
 // Issue order of one ring step, pinned for the scheduler: each of the NV
 // DMA transfers after an MFMA, then the next stage's twelve fragment reads
 // two per MFMA, then the remaining MFMAs -- so the address unit (whose
@@ -93,6 +82,17 @@ __device__ __forceinline__ void interleave() {
   __builtin_amdgcn_sched_group_barrier(0x008, 16 - NV - 6, 0);
 }
 
+// Workgroup = WM x WN wavefronts; wavefront (wm, wn) owns TM x TN blocks of
+// 32 x 32 computed with v_mfma_f32_32x32x16_bf16 (on gfx950 this instruction
+// sustains about 1.6x the rate of the 16x16x32 form), so a tile is
+// 32*TM*WM rows x 32*TN*WN B-columns.  B stages hold the tile's 16-column x
+// 32-K blocks (1 KiB, lane order): a 16 x 32 B operand is read from two
+// adjacent blocks, lane l taking column l % 32 (block (l % 32) / 16, its
+// column l % 16) and K-slot 2s + l / 32 of the stage (substep s = 0, 1), so
+// 16 lanes read 256 contiguous bytes.  A pair slots hold 8-row blocks laid
+// out as described at the staging code; lane l reads row l % 32 and the same
+// K-slot.  The accumulator of lane l holds column l % 32 and rows
+// 8 * (r / 4) + 4 * (l / 32) + r % 4, r < 16.
 template <int MODE, int TM, int TN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
   constexpr int NW = WM * WN;                      // wavefronts
@@ -215,7 +215,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
     // completion makes the waits fixed counts: an even step needs the B
     // stage issued three steps back (2 HB + HA younger transfers), an odd
     // step the A pair issued two steps back (HB younger).  Past the end the
-    // last stage / pair is re-read into slots that are never read again.
+    // last stage / pair is re-read into slots that are never read again, and
+    // the last step's reads of the stage after the last fetch that complete
+    // re-read data into registers that go unused.
     issue_b(0, lb0);
     issue_a(0, pa0);
     issue_b(1, lb1);
