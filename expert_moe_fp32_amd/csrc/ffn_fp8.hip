@@ -378,20 +378,10 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
         lds_dma16(wp + (size_t)kb * 128 + 64 * (b & 1), B + ((b < 2 ? 0 : 8) + wv) * 128 + 64 * (b & 1));
       }
     };
+    constexpr int NT = A_PER + 5;                // transfers per stage
     auto issue = [&](int kb, u32x4_t* A, u32x4_t* B, float* S) {
 #pragma unroll
-      for (int i = 0; i < A_PER; ++i) {
-        lds_dma16(abase + (size_t)arow[i] * K + kb * 128 + achunk[i],
-                  A + aid[i] * 64);
-      }
-      lds_dma16(wp0 + (size_t)kb * 128, B + wv * 128);
-      lds_dma16(wp0 + (size_t)kb * 128 + 64, B + wv * 128 + 64);
-      lds_dma16(wp1 + (size_t)kb * 128, B + (8 + wv) * 128);
-      lds_dma16(wp1 + (size_t)kb * 128 + 64, B + (8 + wv) * 128 + 64);
-      const float* sg = sreal ? sbase + (size_t)srow * KB + kb
-                              : sdump + (size_t)kb * 512;
-      __builtin_amdgcn_global_load_lds(sg, (lds_void*)(S + 64 * (sreal ? wv : NRS)),
-                                       4, 0, 0);
+      for (int i = 0; i < NT; ++i) dma(i, kb, A, B, S);
     };
     constexpr int MH = NMB / 2;                  // row blocks per wavefront
     // the stage's weight slot of this wavefront's block j (DMA order: slot s
@@ -411,7 +401,6 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
     // alternate between two register sets and block m + 1's MFMAs issue
     // before block m's scaling: with one temporary, each MFMA waited for the
     // previous product's scaling and each scaling for its MFMA's result.
-    constexpr int NT = A_PER + 5;                // transfers per stage
     auto compute = [&](int kb, const u32x4_t* A, const u32x4_t* B, const float* S,
                        auto&& xfer) {
       const float ws0 = wscale(w0lo, w0hi, kb);
