@@ -12,9 +12,24 @@
 
 namespace moe {
 
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 static constexpr int kCombineCPT = 4;      // column groups per thread per pass
 
-template <int OUT_BF16>
+// Streaming (large batches): the expert outputs are read once and the output
+// written once, so both go through non-temporal accesses, which keep them
+// from displacing the L2's other lines (prefill combine 123 -> 92 us).
+template <int STREAM, typename V>
+__device__ __forceinline__ V ld(const V* p) {
+  if (STREAM) return __builtin_nontemporal_load(p);
+  return *p;
+}
+template <int STREAM, typename V>
+__device__ __forceinline__ void st(V v, V* p) {
+  if (STREAM) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+template <int OUT_BF16, int STREAM>
 __global__ __launch_bounds__(256) void k_combine(
     const float* __restrict__ y, const int32_t* __restrict__ pair_row,
     const float* __restrict__ w, const float* __restrict__ y_shared, int T,
@@ -44,7 +59,7 @@ __global__ __launch_bounds__(256) void k_combine(
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = cbeg + threadIdx.x + 256 * i;
-    sh0[i] = (ys && c < cend) ? *(const f32x4_t*)(ys + 4 * c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    sh0[i] = (ys && c < cend) ? ld<STREAM>((const f32x4_t*)(ys + 4 * c)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
   const int n = nloc;
@@ -57,7 +72,7 @@ __global__ __launch_bounds__(256) void k_combine(
     for (int i = 0; i < CPT; ++i) {
       const int c = c0 + 256 * i;
       shv[i] = c0 == cbeg + (int)threadIdx.x ? sh0[i]
-               : (ys && c < cend) ? *(const f32x4_t*)(ys + 4 * c)
+               : (ys && c < cend) ? ld<STREAM>((const f32x4_t*)(ys + 4 * c))
                                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     for (int j = 0; j < n; ++j) {
@@ -67,7 +82,7 @@ __global__ __launch_bounds__(256) void k_combine(
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const int c = c0 + 256 * i;
-        v[i] = c < cend ? *(const f32x4_t*)(yr + 4 * c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        v[i] = c < cend ? ld<STREAM>((const f32x4_t*)(yr + 4 * c)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
@@ -86,12 +101,12 @@ __global__ __launch_bounds__(256) void k_combine(
         s.x += shv[i].x; s.y += shv[i].y; s.z += shv[i].z; s.w += shv[i].w;
       }
       if (OUT_BF16) {
-        uint2 pk;
+        u32x2_t pk;
         pk.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
         pk.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
-        *(uint2*)((bf16_t*)out + (size_t)t * H + 4 * c) = pk;
+        st<STREAM>(pk, (u32x2_t*)((bf16_t*)out + (size_t)t * H + 4 * c));
       } else {
-        *(f32x4_t*)((float*)out + (size_t)t * H + 4 * c) = s;
+        st<STREAM>(s, (f32x4_t*)((float*)out + (size_t)t * H + 4 * c));
       }
     }
   }
@@ -108,10 +123,19 @@ hipError_t launch_combine(const float* y_perm, const int32_t* pair_row,
   const int want = T >= 2048 ? 1 : min(groups, (2048 + T - 1) / T);
   const int cw = ((groups + want - 1) / want) * 256;
   const dim3 grid(T, (H4 + cw - 1) / cw);
-  if (out_dtype == MOE_BF16)
-    k_combine<1><<<grid, 256, 0, s>>>(y_perm, pair_row, w, y_shared, T, H, k, cw, out);
-  else
-    k_combine<0><<<grid, 256, 0, s>>>(y_perm, pair_row, w, y_shared, T, H, k, cw, out);
+  // (the decode-sized path reads outputs the expert kernels just left in L2)
+  const bool stream = T >= 2048;
+  if (out_dtype == MOE_BF16) {
+    if (stream)
+      k_combine<1, 1><<<grid, 256, 0, s>>>(y_perm, pair_row, w, y_shared, T, H, k, cw, out);
+    else
+      k_combine<1, 0><<<grid, 256, 0, s>>>(y_perm, pair_row, w, y_shared, T, H, k, cw, out);
+  } else {
+    if (stream)
+      k_combine<0, 1><<<grid, 256, 0, s>>>(y_perm, pair_row, w, y_shared, T, H, k, cw, out);
+    else
+      k_combine<0, 0><<<grid, 256, 0, s>>>(y_perm, pair_row, w, y_shared, T, H, k, cw, out);
+  }
   return hipGetLastError();
 }
 
