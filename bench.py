@@ -68,7 +68,7 @@ TRAFFIC = {
         kernel="k_ring_fp8<0, 10>",
         files=("expert_moe_fp32_amd/csrc/ffn_fp8.hip",
                "expert_moe_fp32_amd/csrc/common.h"),
-        sha="da2fd3e1d5d9fec2", fetch_kib=474092.5, write_kib=33232.0,
+        sha="919aacd5cdd58cb6", fetch_kib=485395.3, write_kib=33232.1,
         fetch_factor=1.9965, write_factor=1.0),
 }
 

@@ -375,7 +375,14 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
       } else {
         const int b = i - 1 - A_PER;
         const u32x4_t* wp = b < 2 ? wp0 : wp1;
-        lds_dma16(wp + (size_t)kb * 128 + 64 * (b & 1), B + ((b < 2 ? 0 : 8) + wv) * 128 + 64 * (b & 1));
+        const void* src = wp + (size_t)kb * 128 + 64 * (b & 1);
+        lds_void* dst = (lds_void*)(B + ((b < 2 ? 0 : 8) + wv) * 128 + 64 * (b & 1));
+        // gate/up weights streamed non-temporally: a routed expert's are
+        // read once (its one tile), and they then do not displace the
+        // activation rows the tile's other column items re-read (gate/up
+        // -3 %; a branch on the group here, to exempt the shared expert,
+        // broke the step's schedule).  Down keeps the default policy.
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, MODE == M8_GATEUP ? 2 : 0);
       }
     };
     constexpr int NT = A_PER + 5;                // transfers per stage
