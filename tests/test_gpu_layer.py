@@ -67,6 +67,9 @@ def sample_tokens(T, n, seed=0):
     # tile list (ring GEMM + 128-row down list; fp32 kernel)
     ("prefill", dict(T=1100, H=384, I=256, E=8, num_local=8, k=2)),
     ("tiny", dict(T=1500, E=16, num_local=8, k=2)),
+    # 2048 tokens or more: the combine's streaming (non-temporal) form, here
+    # with float32 output
+    ("tiny", dict(T=2100, E=16, num_local=8, k=2)),
     # ring GEMM with the shortest reductions it takes (K = 128, one trip of
     # its 4-stage loop: prologue, register prefetch and clamped tail
     # transfers only): down with I = 128, gate/up with H = 128
