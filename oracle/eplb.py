@@ -19,8 +19,10 @@ local experts, tokens split round-robin) is ``hottest_replica_map``.
 from __future__ import annotations
 
 import bisect
+import heapq
 import itertools
 import random
+from fractions import Fraction
 from typing import List, Sequence, Tuple
 
 import numpy as np
@@ -57,30 +59,48 @@ def replica_share(n: int, R: int) -> List[int]:
 
 
 # ------------------------------------------------ the load simulation (5.2)
-def simulate_expert_counts(seed: int = 0, experts: int = 256, top_k: int = 8,
-                           tokens: int = 4096, skew: float = 0.4) -> List[int]:
-    """Token counts per expert under power-law popularity.
+def simulate_routing(seed: int = 0, experts: int = 256, top_k: int = 8,
+                     tokens: int = 4096, skew: float = 0.4):
+    """Per-token expert picks under power-law popularity, and the counts.
 
-    Expert i (before shuffling) has popularity 1/(i+1)^skew; the popularity
-    list is shuffled with Python's seeded Mersenne Twister; each token then
-    draws experts with probability proportional to popularity, one draw at a
-    time, until it holds ``top_k`` distinct ones.  A weighted draw is the
-    inverse-CDF lookup of one uniform variate in the cumulative popularity
-    (the same sampling ``random.choices`` performs)."""
+    The model of section 5.2: expert i (before shuffling) is popular in
+    proportion to 1/(i+1)^skew; the popularity list is shuffled so hot
+    experts land on scattered ids; every token then draws experts one at a
+    time, with probability proportional to popularity, until it holds
+    ``top_k`` distinct ones.
+
+    Sampling contract (the only part kept in step with the page's script,
+    because its printed counts can be reproduced in no other way): one
+    Python ``random.Random(seed)`` stream, consumed first by the shuffle and
+    then by one uniform variate per draw, and a draw maps its variate u to
+    the first expert whose cumulative popularity exceeds u * total -- the
+    inverse-CDF lookup that ``random.choices`` performs.
+
+    Returns (picks [tokens][top_k] with each token's experts in ascending
+    id order, counts [experts])."""
     rng = random.Random(seed)
     pop = [1.0 / (i + 1) ** skew for i in range(experts)]
     rng.shuffle(pop)
     cum = list(itertools.accumulate(pop))
     total = cum[-1] + 0.0
-    counts = [0] * experts
+    picks: List[List[int]] = []
     for _ in range(tokens):
-        picked = set()
-        while len(picked) < top_k:
-            picked.add(bisect.bisect(cum, rng.random() * total, 0,
-                                     experts - 1))
-        for e in picked:
+        held = set()
+        while len(held) < top_k:
+            held.add(bisect.bisect(cum, rng.random() * total, 0,
+                                   experts - 1))
+        picks.append(sorted(held))
+    counts = [0] * experts
+    for row in picks:
+        for e in row:
             counts[e] += 1
-    return counts
+    return picks, counts
+
+
+def simulate_expert_counts(seed: int = 0, experts: int = 256, top_k: int = 8,
+                           tokens: int = 4096, skew: float = 0.4) -> List[int]:
+    """Token counts per expert of ``simulate_routing``."""
+    return simulate_routing(seed, experts, top_k, tokens, skew)[1]
 
 
 def contiguous_load(counts: Sequence[int], ep: int) -> List[float]:
@@ -90,39 +110,52 @@ def contiguous_load(counts: Sequence[int], ep: int) -> List[float]:
 
 
 def plan_replicas(counts: Sequence[int], redundant: int) -> List[int]:
-    """Replica count per expert: each extra replica goes to the expert with
-    the highest load per replica at that moment (lower id on ties)."""
+    """Replica count per expert (section 5.2's rule): every redundant slot,
+    one at a time, goes to the expert whose load per replica is highest at
+    that moment; among equal loads per replica the lower id wins.
+
+    A priority queue holds each expert keyed by its exact load per replica
+    (a ``Fraction``, so no rounding decides a tie); the granted expert goes
+    back in with its new, lower key."""
     rep = [1] * len(counts)
+    queue = [(-Fraction(int(c)), e) for e, c in enumerate(counts)]
+    heapq.heapify(queue)
     for _ in range(redundant):
-        best = 0
-        for e in range(1, len(counts)):
-            if counts[e] * rep[best] > counts[best] * rep[e]:
-                best = e
-        rep[best] += 1
+        _, e = heapq.heappop(queue)
+        rep[e] += 1
+        heapq.heappush(queue, (-Fraction(int(counts[e]), rep[e]), e))
     return rep
 
 
 def place_replicas(counts: Sequence[int], replicas: Sequence[int], ep: int
                    ) -> Tuple[List[List[Tuple[int, int]]], List[float]]:
-    """Place every replica (load counts[e]/replicas[e]) heaviest first onto the
-    lightest rank with a free slot (lower rank on ties); each rank has
-    (total replicas) / ep slots.  Equal loads are taken in (expert, replica)
-    order.  Returns per rank the list of (expert, replica index) and the rank
-    loads."""
+    """Placement of every replica (section 5.2's rule): a replica carries
+    load counts[e] / replicas[e]; replicas are taken heaviest first and each
+    goes to the currently lightest rank that still has a free slot.  Every
+    rank has (total replicas) / ep slots (section 5.3's (E + R) / EP).
+
+    Order among equal loads: replicas in (expert, replica) order; among
+    equally light ranks the lower rank.  The open ranks sit in a priority
+    queue keyed (load, rank); a rank leaves it when its slots are full.
+    Returns per rank the list of (expert, replica index) it holds, in
+    placement order, and the rank loads (float sums in placement order)."""
     total = sum(replicas)
     if total % ep:
         raise ValueError("total replicas must divide evenly over the ranks")
     slots = total // ep
-    copies = [(counts[e] / replicas[e], e, r)
-              for e in range(len(counts)) for r in range(replicas[e])]
-    copies.sort(key=lambda c: (-c[0], c[1], c[2]))
+    order = sorted(((e, r) for e in range(len(counts))
+                    for r in range(replicas[e])),
+                   key=lambda er: (-Fraction(int(counts[er[0]]),
+                                             replicas[er[0]]),) + er)
     load = [0.0] * ep
     held: List[List[Tuple[int, int]]] = [[] for _ in range(ep)]
-    for w, e, r in copies:
-        g = min((g for g in range(ep) if len(held[g]) < slots),
-                key=lambda g: (load[g], g))
-        load[g] += w
+    open_ranks = [(0.0, g) for g in range(ep)] if slots else []
+    for e, r in order:
+        _, g = heapq.heappop(open_ranks)
+        load[g] += counts[e] / replicas[e]
         held[g].append((e, r))
+        if len(held[g]) < slots:
+            heapq.heappush(open_ranks, (load[g], g))
     return held, load
 
 
