@@ -21,11 +21,15 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, \
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
+MOE_LAYOUT_KN, MOE_LAYOUT_NK = range(2)
+LAYOUTS = {"kn": MOE_LAYOUT_KN, "nk": MOE_LAYOUT_NK}
+
 EXPORTS = (
-    "moe_status_string", "moe_check_problem", "moe_dispatch_workspace_size",
+    "moe_status_string", "moe_check_problem", "moe_workspace_size",
+    "moe_dispatch_workspace_size",
     "moe_ffn_workspace_size", "moe_layer_workspace_size", "moe_route_topk",
-    "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-    "moe_layer_forward_timed", "moe_prepack_weights",
+    "moe_dispatch", "moe_grouped_ffn", "moe_ffn_intermediate", "moe_combine",
+    "moe_layer_forward", "moe_layer_forward_timed", "moe_prepack_weights",
     "moe_quantize_fp8_blocks",
     "moe_eplb_hottest_map", "moe_eplb_plan", "moe_eplb_rank_map",
     "moe_eplb_record_load",
@@ -71,6 +75,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "moe_check_problem": (ctypes.c_int, [P]),
+            "moe_workspace_size": (ctypes.c_int, [P, ctypes.POINTER(S)]),
             "moe_dispatch_workspace_size": (ctypes.c_int, [P, ctypes.POINTER(S)]),
             "moe_ffn_workspace_size": (ctypes.c_int, [P, ctypes.POINTER(S)]),
             "moe_layer_workspace_size": (ctypes.c_int, [P, ctypes.POINTER(S)]),
@@ -80,6 +85,8 @@ def lib() -> ctypes.CDLL:
             "moe_grouped_ffn": (ctypes.c_int, [P, V, V, V, V, V,
                                                ctypes.POINTER(Weights), V, V,
                                                V, S, V]),
+            "moe_ffn_intermediate": (ctypes.c_int, [
+                P, V, S, ctypes.POINTER(V), ctypes.POINTER(V)]),
             "moe_combine": (ctypes.c_int, [P, V, V, V, V, V, V]),
             "moe_layer_forward": (ctypes.c_int, [P, V, V, V,
                                                  ctypes.POINTER(Weights), V, V,
@@ -88,9 +95,10 @@ def lib() -> ctypes.CDLL:
                                                        ctypes.POINTER(Weights),
                                                        V, V, V, V, V, S, V,
                                                        V]),
-            "moe_prepack_weights": (ctypes.c_int, [V, I32, I32, I32, V, V]),
-            "moe_quantize_fp8_blocks": (ctypes.c_int, [V, I32, I32, I32, V, V,
-                                                       V]),
+            "moe_prepack_weights": (ctypes.c_int, [V, I32, I32, I32, I32, V,
+                                                   V]),
+            "moe_quantize_fp8_blocks": (ctypes.c_int, [V, I32, I32, I32, I32,
+                                                       V, V, V]),
             "moe_eplb_hottest_map": (ctypes.c_int, [V, I32, I32, V, V, V]),
             "moe_eplb_plan": (ctypes.c_int, [V, I32, I32, I32, V, V, V, V]),
             "moe_eplb_rank_map": (ctypes.c_int, [V, V, V, I32, I32, I32, I32,
@@ -153,6 +161,10 @@ def _ws(fn, p: Problem) -> int:
     return n.value
 
 
+def moe_workspace_size(p: Problem) -> int:
+    return _ws(lib().moe_workspace_size, p)
+
+
 def moe_dispatch_workspace_size(p: Problem) -> int:
     return _ws(lib().moe_dispatch_workspace_size, p)
 
@@ -201,6 +213,18 @@ def moe_grouped_ffn(p, x_perm, x_perm_scales, offsets, x_shared,
     return st
 
 
+def moe_ffn_intermediate(p, workspace, ws_bytes):
+    """Device addresses (h, h_scales or None) of the expert intermediate
+    inside an FFN workspace."""
+    h = ctypes.c_void_p()
+    hs = ctypes.c_void_p()
+    _check(lib().moe_ffn_intermediate(ctypes.byref(p), ptr(workspace),
+                                      ws_bytes, ctypes.byref(h),
+                                      ctypes.byref(hs)),
+           "moe_ffn_intermediate")
+    return h.value, hs.value
+
+
 def moe_combine(p, y_perm, pair_row, topk_w, y_shared, out, stream=None,
                 check=True) -> int:
     st = lib().moe_combine(ctypes.byref(p), ptr(y_perm), ptr(pair_row),
@@ -240,20 +264,22 @@ def moe_layer_forward_timed(p, logits, bias, x, weights: Weights, l2p,
     return st
 
 
-def moe_prepack_weights(src, rows, cols, dtype, dst, stream=None,
+def moe_prepack_weights(src, K, N, dtype, layout, dst, stream=None,
                         check=True) -> int:
+    """Prepare a K x N weight matrix stored ``layout`` (MOE_LAYOUT_KN =
+    [K][N], MOE_LAYOUT_NK = [N][K]) into the form moe_weights takes."""
     st = lib().moe_prepack_weights(
-        ptr(src), rows, cols, dtype, ptr(dst),
+        ptr(src), K, N, dtype, layout, ptr(dst),
         stream if stream is not None else current_stream())
     if check:
         _check(st, "moe_prepack_weights")
     return st
 
 
-def moe_quantize_fp8_blocks(w, rows, cols, block, codes, scales, stream=None,
-                            check=True) -> int:
+def moe_quantize_fp8_blocks(w, K, N, block, layout, codes, scales,
+                            stream=None, check=True) -> int:
     st = lib().moe_quantize_fp8_blocks(
-        ptr(w), rows, cols, block, ptr(codes), ptr(scales),
+        ptr(w), K, N, block, layout, ptr(codes), ptr(scales),
         stream if stream is not None else current_stream())
     if check:
         _check(st, "moe_quantize_fp8_blocks")

@@ -321,6 +321,33 @@ moe_status moe_layer_workspace_size(const moe_problem* p, size_t* bytes) {
   return MOE_OK;
 }
 
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
+  moe_status st = moe_check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+  size_t d = 0, f = 0, l = 0;
+  moe_dispatch_workspace_size(p, &d);
+  moe_ffn_workspace_size(p, &f);
+  moe_layer_workspace_size(p, &l);
+  *bytes = std::max(d, std::max(f, l));
+  return MOE_OK;
+}
+
+moe_status moe_ffn_intermediate(const moe_problem* p, void* workspace,
+                                size_t ws_bytes, void** h, float** h_scales) {
+  moe_status st = moe_check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!h || !h_scales) return MOE_ERR_INVALID_ARGUMENT;
+  size_t need;
+  moe_ffn_workspace_size(p, &need);
+  if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  Carver c(workspace);
+  FfnScratch fs = carve_ffn(c, p);
+  *h = fs.h;
+  *h_scales = p->weight_dtype == MOE_FP8_E4M3 ? fs.h_scales : nullptr;
+  return MOE_OK;
+}
+
 moe_status moe_route_topk(const moe_problem* p, const float* logits,
                           const float* bias, int32_t* topk_ids, float* topk_w,
                           int32_t* expert_counts, void* stream) {
@@ -503,28 +530,34 @@ moe_status moe_layer_forward_timed(const moe_problem* p, const float* logits,
                     expert_counts, workspace, ws_bytes, stream, ev);
 }
 
-moe_status moe_prepack_weights(const void* src, int32_t rows, int32_t cols,
-                               int32_t dtype, void* dst, void* stream) {
-  if (rows < 0 || cols < 0) return MOE_ERR_INVALID_ARGUMENT;
-  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
-  const int cblk = dtype == MOE_BF16 ? 32 : 128;
-  if (rows % 16 || cols % cblk) return MOE_ERR_INVALID_ARGUMENT;
-  if (rows == 0 || cols == 0) return MOE_OK;
+moe_status moe_prepack_weights(const void* src, int32_t K, int32_t N,
+                               int32_t dtype, int32_t layout, void* dst,
+                               void* stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_FP8_E4M3)
+    return MOE_ERR_UNSUPPORTED;
+  if (layout != MOE_LAYOUT_KN && layout != MOE_LAYOUT_NK)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (K < 0 || N < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (dtype == MOE_BF16 && (N % 16 || K % 32)) return MOE_ERR_INVALID_ARGUMENT;
+  if (dtype == MOE_FP8_E4M3 && (N % 16 || K % 128))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (K == 0 || N == 0) return MOE_OK;
   if (!src || !dst || src == dst) return MOE_ERR_INVALID_ARGUMENT;
-  if (dtype == MOE_FP8_E4M3)
-    return hip_status(launch_pack_fp8((const uint8_t*)src, rows, cols, dst, S(stream)));
-  return hip_status(launch_pack_bf16((const bf16_t*)src, rows, cols, dst, S(stream)));
+  return hip_status(launch_prepack(src, K, N, dtype, layout, dst, S(stream)));
 }
 
-moe_status moe_quantize_fp8_blocks(const float* w, int32_t rows, int32_t cols,
-                                   int32_t block, uint8_t* codes,
-                                   float* scales, void* stream) {
+moe_status moe_quantize_fp8_blocks(const float* w, int32_t K, int32_t N,
+                                   int32_t block, int32_t layout,
+                                   uint8_t* codes, float* scales,
+                                   void* stream) {
   if (block != 128) return MOE_ERR_UNSUPPORTED;
-  if (rows < 0 || cols < 0 || rows % block || cols % block)
+  if (layout != MOE_LAYOUT_KN && layout != MOE_LAYOUT_NK)
     return MOE_ERR_INVALID_ARGUMENT;
-  if (rows == 0 || cols == 0) return MOE_OK;
+  if (K < 0 || N < 0 || K % block || N % block) return MOE_ERR_INVALID_ARGUMENT;
+  if (K == 0 || N == 0) return MOE_OK;
   if (!w || !codes || !scales) return MOE_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_quant_blocks_fp8(w, rows, cols, codes, scales, S(stream)));
+  return hip_status(
+      launch_quant_blocks_fp8(w, K, N, layout, codes, scales, S(stream)));
 }
 
 }  // extern "C"

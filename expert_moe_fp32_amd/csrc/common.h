@@ -161,7 +161,9 @@ hipError_t launch_gather_rows_words(const void* x, int row_words,
 hipError_t launch_quant_rows_fp8(const bf16_t* x, int T, int H,
                                  uint8_t* codes, float* scales, hipStream_t s);
 
-hipError_t launch_quant_blocks_fp8(const float* w, int rows, int cols,
+// FP8 block quantisation of a float32 matrix stored KN ([K][N]) or NK
+// ([N][K]); codes in the source's order, scales [N/128][K/128]
+hipError_t launch_quant_blocks_fp8(const float* w, int K, int N, int layout,
                                    uint8_t* codes, float* scales,
                                    hipStream_t s);
 
@@ -212,11 +214,9 @@ hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
                               int T, int BM, int balanced, int4* tiles,
                               int32_t* count, hipStream_t s);
 
-// natural output-major [R][C] -> packed operand blocks (bf16: 16x32 blocks;
-// fp8: 16x128 blocks)
-hipError_t launch_pack_bf16(const bf16_t* src, int R, int C, void* dst,
-                            hipStream_t s);
-hipError_t launch_pack_fp8(const uint8_t* src, int R, int C, void* dst,
-                           hipStream_t s);
+// a K x N matrix stored KN or NK -> its prepared form for `dtype` (float32
+// [K][N]; bf16 16x32 or fp8 16x128 packed operand blocks)
+hipError_t launch_prepack(const void* src, int K, int N, int dtype, int layout,
+                          void* dst, hipStream_t s);
 
 }  // namespace moe

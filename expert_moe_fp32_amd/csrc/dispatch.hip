@@ -109,7 +109,10 @@ __global__ __launch_bounds__(256) void k_local_hist(
     for (int e = threadIdx.x; e < E; e += blockDim.x) ehist[e] = 0;
     __syncthreads();
     if (t < T)
-      for (int j = 0; j < k; ++j) atomicAdd(&ehist[ids[(size_t)t * k + j]], 1);
+      for (int j = 0; j < k; ++j) {       // ids outside [0, E): not counted
+        const int gid = ids[(size_t)t * k + j];
+        if ((unsigned)gid < (unsigned)E) atomicAdd(&ehist[gid], 1);
+      }
   }
   int le[MOE_KMAX];
   load_local_ids(ids, t, T, k, e0, L, le);
@@ -321,7 +324,8 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
     if (j < k && t < T) {
       const int gid = a.ids[(size_t)t * k + j];
       wj[j] = a.w[(size_t)t * k + j];
-      atomicAdd(&cnt[gid], 1);
+      // expert counts only when asked for, and only of ids in [0, E)
+      if (x.counts && (unsigned)gid < (unsigned)x.E) atomicAdd(&cnt[gid], 1);
       const int e = gid - a.expert_begin;
       if (e >= 0 && e < L) le[j] = e;
     }
@@ -523,40 +527,6 @@ hipError_t launch_quant_rows_fp8(const bf16_t* x, int T, int H,
   if (n8 == 0) return hipSuccess;
   k_quant_rows_fp8<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(x, n8, codes,
                                                                scales);
-  return hipGetLastError();
-}
-
-// One workgroup per 128x128 block of a float32 matrix.
-__global__ __launch_bounds__(256) void k_quant_blocks_fp8(
-    const float* __restrict__ w, int rows, int cols,
-    uint8_t* __restrict__ codes, float* __restrict__ scales) {
-  __shared__ float red[4];
-  const int bc = cols / 128;
-  const int bi = blockIdx.x / bc, bj = blockIdx.x % bc;
-  const float* base = w + (size_t)bi * 128 * cols + (size_t)bj * 128;
-  float amax = 0.0f;
-  for (int i = threadIdx.x; i < 128 * 128; i += 256)
-    amax = fmaxf(amax, fabsf(base[(size_t)(i >> 7) * cols + (i & 127)]));
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float sc = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
-  uint8_t* cb = codes + (size_t)bi * 128 * cols + (size_t)bj * 128;
-  for (int i = threadIdx.x; i < 128 * 128; i += 256) {
-    const size_t o = (size_t)(i >> 7) * cols + (i & 127);
-    cb[o] = f32_to_e4m3(__fdiv_rn(base[o], sc));
-  }
-  if (threadIdx.x == 0) scales[blockIdx.x] = sc;
-}
-
-hipError_t launch_quant_blocks_fp8(const float* w, int rows, int cols,
-                                   uint8_t* codes, float* scales,
-                                   hipStream_t s) {
-  const int nb = (rows / 128) * (cols / 128);
-  if (nb == 0) return hipSuccess;
-  k_quant_blocks_fp8<<<nb, 256, 0, s>>>(w, rows, cols, codes, scales);
   return hipGetLastError();
 }
 

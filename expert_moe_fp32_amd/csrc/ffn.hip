@@ -10,13 +10,14 @@
 // with no rows owns none and its weights are never read.
 //
 // bf16 weights arrive in the packed operand layout written by
-// moe_prepack_weights: a matrix stored output-major [R][C] (C = reduction) is
-// cut into 16 x 32 blocks, block (r/16, c/32) stored at block index
-// (r/16) * (C/32) + c/32, 1 KiB each, and inside a block lane
-// L = r%16 + 16 * ((c%32)/8) holds the 8 consecutive values c%8 = 0..7.  A
-// block is exactly one wavefront's operand of v_mfma_f32_16x16x32_bf16, so a
-// 16-B load per lane reads 1 KiB of contiguous memory, and 16 output
-// channels over the whole reduction are one contiguous run.
+// moe_prepack_weights (prepare.hip): a matrix with reduction size K and N
+// output channels is cut into blocks of 16 channels x 32 reduction values,
+// block (n/16, k/32) stored at block index (n/16) * (K/32) + k/32, 1 KiB
+// each, and inside a block lane L = n%16 + 16 * ((k%32)/8) holds the 8
+// consecutive values k%8 = 0..7.  A block is exactly one wavefront's operand
+// of v_mfma_f32_16x16x32_bf16, so a 16-B load per lane reads 1 KiB of
+// contiguous memory, and 16 output channels over the whole reduction are one
+// contiguous run.
 //
 // bf16 kernels on the tile list:
 //  * k_stream_bf16 (groups of a few rows, decode): each wavefront streams its
@@ -347,70 +348,107 @@ __global__ __launch_bounds__(256) void k_tile_bf16_down(KArgs a) {
 }
 
 // --------------------------------------------------------- fp32 recipe
-// Plain float32 FMA kernels on natural output-major weights: one thread per
-// (row, output channel).
+// Float32 weights in the logical layout [K][N] (gate/up [H][I], down [I][H]).
+// A workgroup computes a 64-row x 64-output tile (both gate and up for
+// gate/up) with float32 FMAs: per 32-deep K step it stages the tile's
+// activation rows (gathered through a_rows) transposed into LDS and the
+// weight rows W[k][n0 .. n0+64) as they lie in memory, both with consecutive
+// threads on consecutive addresses; each thread then accumulates 4 rows x 4
+// outputs in registers, in ascending k.
+static constexpr int F32_BM = 64, F32_BN = 64, F32_BK = 32;
+
 template <int MODE>
 __global__ __launch_bounds__(256) void k_f32(KArgs a) {
-  const int total_tiles = a.tile_count[0];
-  const long per_tile = (long)TBM * a.N;    // tiles of up to TBM rows
-  const long total = (long)total_tiles * per_tile;
-  for (long it = (long)blockIdx.x * blockDim.x + threadIdx.x; it < total;
-       it += (long)gridDim.x * blockDim.x) {
-    const int tile = (int)(it / per_tile);
-    const int rem = (int)(it - (long)tile * per_tile);
-    const int r = rem / a.N, n = rem - r * a.N;
+  __shared__ float As[F32_BK][F32_BM + 4];
+  __shared__ float Ws0[F32_BK][F32_BN];
+  __shared__ float Ws1[MODE == MODE_GATEUP ? F32_BK : 1][F32_BN];
+  const int tid = threadIdx.x;
+  const int ty = tid >> 4, tx = tid & 15;      // 4 rows x 4 outputs each
+  const int K = a.K, N = a.N;
+  const int total = a.tile_count[0] * a.nb_per_tile;
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int tile = item / a.nb_per_tile;
+    const int nb = item - tile * a.nb_per_tile;
     const int4 td = a.tiles[tile];
-    if (r >= td.z) continue;
-    const int g = td.x, row = td.y + r;
+    const int g = td.x, row0 = td.y, nrows = td.z;
     const bool sh = g == a.P;
-    const float* A;
-    if (sh) A = (const float*)a.a_shared + (size_t)row * a.K;
-    else A = (const float*)a.a_routed + (size_t)(a.a_rows ? a.a_rows[row] : row) * a.K;
-    const float* W0 = (const float*)(sh ? a.w0_sh : a.w0_arr[g]) + (size_t)n * a.K;
-    if (MODE == MODE_GATEUP) {
-      const float* W1 = (const float*)(sh ? a.w1_sh : a.w1_arr[g]) + (size_t)n * a.K;
-      float gs = 0.f, us = 0.f;
-      for (int kk = 0; kk < a.K; ++kk) {
-        gs = __builtin_fmaf(A[kk], W0[kk], gs);
-        us = __builtin_fmaf(A[kk], W1[kk], us);
+    const int n0 = nb * F32_BN;
+    const float* W0 = (const float*)(sh ? a.w0_sh : a.w0_arr[g]);
+    const float* W1 = MODE == MODE_GATEUP
+                          ? (const float*)(sh ? a.w1_sh : a.w1_arr[g])
+                          : nullptr;
+    // the activation row each of this thread's staging slots reads
+    const float* arow[F32_BM * F32_BK / 256];
+#pragma unroll
+    for (int i = 0; i < F32_BM * F32_BK / 256; ++i) {
+      const int m = (tid + 256 * i) / F32_BK;
+      const int r = row0 + (m < nrows ? m : 0);
+      arow[i] = sh ? (const float*)a.a_shared + (size_t)r * K
+                   : (const float*)a.a_routed +
+                         (size_t)(a.a_rows ? a.a_rows[r] : r) * K;
+    }
+    float acc0[4][4], acc1[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc0[i][j] = acc1[i][j] = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += F32_BK) {
+      __syncthreads();                         // previous step's readers
+#pragma unroll
+      for (int i = 0; i < F32_BM * F32_BK / 256; ++i) {
+        const int idx = tid + 256 * i;
+        const int m = idx / F32_BK, kk = idx % F32_BK;
+        As[kk][m] = (m < nrows && k0 + kk < K) ? arow[i][k0 + kk] : 0.0f;
       }
-      const size_t hr = (size_t)(sh ? a.cap : 0) + row;
-      ((float*)a.h_out)[hr * a.N + n] = silu_f32(gs) * us;
-    } else {
-      float ys = 0.f;
-      for (int kk = 0; kk < a.K; ++kk) ys = __builtin_fmaf(A[kk], W0[kk], ys);
-      float* y = sh ? a.y_shared : a.y_routed;
-      y[(size_t)row * a.N + n] = ys;
+#pragma unroll
+      for (int i = 0; i < F32_BK * F32_BN / 256; ++i) {
+        const int idx = tid + 256 * i;
+        const int kk = idx / F32_BN, nn = idx % F32_BN;
+        const bool in = k0 + kk < K && n0 + nn < N;
+        const size_t o = (size_t)(k0 + kk) * N + n0 + nn;
+        Ws0[kk][nn] = in ? W0[o] : 0.0f;
+        if (MODE == MODE_GATEUP) Ws1[kk][nn] = in ? W1[o] : 0.0f;
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int kk = 0; kk < F32_BK; ++kk) {
+        float av[4], b0[4], b1[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          b0[j] = Ws0[kk][tx * 4 + j];
+          if (MODE == MODE_GATEUP) b1[j] = Ws1[kk][tx * 4 + j];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc0[i][j] = __builtin_fmaf(av[i], b0[j], acc0[i][j]);
+            if (MODE == MODE_GATEUP)
+              acc1[i][j] = __builtin_fmaf(av[i], b1[j], acc1[i][j]);
+          }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = ty * 4 + i;
+      if (r >= nrows) continue;
+      const int row = row0 + r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + tx * 4 + j;
+        if (n >= N) continue;
+        if (MODE == MODE_GATEUP) {
+          const size_t hr = (size_t)(sh ? a.cap : 0) + row;
+          ((float*)a.h_out)[hr * N + n] = silu_f32(acc0[i][j]) * acc1[i][j];
+        } else {
+          float* y = sh ? a.y_shared : a.y_routed;
+          y[(size_t)row * N + n] = acc0[i][j];
+        }
+      }
     }
   }
-}
-
-// ------------------------------------------------------- weight packing
-// Natural output-major bf16 [R][C] -> packed 16 x 32 operand blocks (see the
-// top of this file).  One thread per 16-byte output chunk.
-__global__ __launch_bounds__(256) void k_pack_bf16(const bf16_t* __restrict__ src,
-                                                   int R, int C,
-                                                   u32x4_t* __restrict__ dst) {
-  const size_t total = (size_t)R * C / 8;
-  const int CB = C / 32;
-  for (size_t gi = (size_t)blockIdx.x * 256 + threadIdx.x; gi < total;
-       gi += (size_t)gridDim.x * 256) {
-    const size_t blk = gi >> 6;
-    const int lane = (int)(gi & 63);
-    const size_t rb = blk / CB, cb = blk - rb * CB;
-    const size_t r = rb * 16 + (lane & 15), c = cb * 32 + (lane >> 4) * 8;
-    dst[gi] = *(const u32x4_t*)(src + r * C + c);
-  }
-}
-
-hipError_t launch_pack_bf16(const bf16_t* src, int R, int C, void* dst,
-                            hipStream_t s) {
-  const size_t total = (size_t)R * C / 8;
-  if (total == 0) return hipSuccess;
-  size_t grid = (total + 255) / 256;
-  if (grid > 8192) grid = 8192;
-  k_pack_bf16<<<(unsigned)grid, 256, 0, s>>>(src, R, C, (u32x4_t*)dst);
-  return hipGetLastError();
 }
 
 // -------------------------------------------------------------- driver
@@ -423,7 +461,7 @@ static bool bf16_streaming(int rows_hint) { return rows_hint <= 32; }
 int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int I, int* balanced) {
   *balanced = 0;
   if (wdt == MOE_FP8_E4M3) return ffn_fp8_tile_rows(rows_hint, H, I, balanced);
-  if (act == MOE_F32) return TBM;
+  if (act == MOE_F32) return F32_BM;
   if (bf16_streaming(rows_hint)) return 32;
   *balanced = 1;
   return gemm_tile_rows();
@@ -485,9 +523,9 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   a.h_out = f.h;
   const int cu = 256;
   if (f32) {
-    long work = max_tiles * TBM * (long)a.N;
-    long grid = (work + 255) / 256;
-    if (grid > cu * 8) grid = cu * 8;
+    a.nb_per_tile = (a.N + F32_BN - 1) / F32_BN;
+    long items = max_tiles * a.nb_per_tile;
+    long grid = items < cu * 4 ? items : cu * 4;
     k_f32<MODE_GATEUP><<<(unsigned)grid, 256, 0, s>>>(a);
   } else if (stream) {
     a.nb_per_tile = a.N / 64;
@@ -516,9 +554,9 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   a.y_routed = f.y_routed;
   a.y_shared = f.y_shared;
   if (f32) {
-    long work = max_tiles * TBM * (long)a.N;
-    long grid = (work + 255) / 256;
-    if (grid > cu * 8) grid = cu * 8;
+    a.nb_per_tile = (a.N + F32_BN - 1) / F32_BN;
+    long items = max_tiles * a.nb_per_tile;
+    long grid = items < cu * 4 ? items : cu * 4;
     k_f32<MODE_DOWN><<<(unsigned)grid, 256, 0, s>>>(a);
   } else if (stream) {
     a.nb_per_tile = a.N / 128;                // two 64-apart blocks per wave

@@ -12,13 +12,15 @@
 // float32 accumulator as acc += sum * s_act[row] * s_w[block] (the MFMA's own
 // power-of-two scale inputs are left at 1).
 //
-// Packed FP8 weight layout (moe_prepack_weights with MOE_FP8_E4M3): a matrix
-// [R][C] of codes (C = reduction) is cut into 16 x 128 blocks of 2 KiB, block
-// (r/16, c/128) stored at block index (r/16) * (C/128) + c/128.  Lane
-// L = r%16 + 16 * ((c%128)/32) owns the 32 codes of its K-slot; their first
+// Packed FP8 weight layout (moe_prepack_weights with MOE_FP8_E4M3, in
+// prepare.hip): a matrix of codes with reduction size K and N output
+// channels is cut into blocks of 16 channels x 128 reduction values, 2 KiB,
+// block (n/16, k/128) stored at block index (n/16) * (K/128) + k/128.  Lane
+// L = n%16 + 16 * ((k%128)/32) owns the 32 codes of its K-slot; their first
 // 16 bytes sit at byte L*16 of the block and the next 16 at 1024 + L*16, so
 // each half of a wavefront's operand is 1 KiB of contiguous memory and a
-// conflict-free 16-byte LDS read per lane.
+// conflict-free 16-byte LDS read per lane.  Weight scales are
+// [N/128][K/128].
 #include "common.h"
 
 namespace moe {
@@ -766,34 +768,6 @@ __global__ __launch_bounds__(256) void k_quant_h_fp8(
     *(uint2*)(codes + hr * I + 8 * ci) = make_uint2(lo, hi);
     if ((threadIdx.x & 15) == 0) scales[hr * (I / 128) + ci / 16] = sc;
   }
-}
-
-// Natural E4M3 codes [R][C] -> packed blocks (top of this file).
-__global__ __launch_bounds__(256) void k_pack_fp8(const uint8_t* __restrict__ src,
-                                                  int R, int C,
-                                                  u32x4_t* __restrict__ dst) {
-  const size_t total = (size_t)R * C / 16;
-  const int CB = C / 128;
-  for (size_t gi = (size_t)blockIdx.x * 256 + threadIdx.x; gi < total;
-       gi += (size_t)gridDim.x * 256) {
-    const size_t blk = gi >> 7;
-    const int idx = (int)(gi & 127);
-    const int L = idx & 63, half = idx >> 6;
-    const size_t rb = blk / CB, cb = blk - rb * CB;
-    const size_t r = rb * 16 + (L & 15);
-    const size_t c = cb * 128 + 32 * (L >> 4) + 16 * half;
-    dst[gi] = *(const u32x4_t*)(src + r * C + c);
-  }
-}
-
-hipError_t launch_pack_fp8(const uint8_t* src, int R, int C, void* dst,
-                           hipStream_t s) {
-  const size_t total = (size_t)R * C / 16;
-  if (total == 0) return hipSuccess;
-  size_t grid = (total + 255) / 256;
-  if (grid > 8192) grid = 8192;
-  k_pack_fp8<<<(unsigned)grid, 256, 0, s>>>(src, R, C, (u32x4_t*)dst);
-  return hipGetLastError();
 }
 
 // Tile rows of the FP8 recipe for an expected group size: the

@@ -119,15 +119,20 @@ __global__ __launch_bounds__(1024) void k_count_ids(
   const bool aligned = ((uintptr_t)ids & 15) == 0;   // 16-B loads need it
   const int n4 = aligned ? n >> 2 : 0;
   const int4* ids4 = (const int4*)ids;
+  // ids outside [0, E) are not counted (they never come from the router,
+  // but a stray one must not write past the histogram)
+  auto count = [&](int e) {
+    if ((unsigned)e < (unsigned)E) atomicAdd(&mine[e], 1);
+  };
 #pragma unroll 4
   for (int i = tid; i < n4; i += 1024) {
     const int4 v = ids4[i];
-    atomicAdd(&mine[v.x], 1);
-    atomicAdd(&mine[v.y], 1);
-    atomicAdd(&mine[v.z], 1);
-    atomicAdd(&mine[v.w], 1);
+    count(v.x);
+    count(v.y);
+    count(v.z);
+    count(v.w);
   }
-  for (int i = 4 * n4 + tid; i < n; i += 1024) atomicAdd(&mine[ids[i]], 1);
+  for (int i = 4 * n4 + tid; i < n; i += 1024) count(ids[i]);
   __syncthreads();
   for (int e = tid; e < E; e += 1024) {
     int c = 0;

@@ -55,9 +55,11 @@ class LayerBuffers:
 class DeviceLayer:
     """One EP rank's MoE layer with weights resident on the device.
 
-    experts: per physical-expert source, a dict of host arrays wg [I,H],
-    wu [I,H], wd [H,I] (float32 for the fp32 and fp8 recipes -- fp8 weights
-    are quantised on the device by moe_quantize_fp8_blocks -- or bf16 bits).
+    experts: per physical-expert source, a dict of host arrays wg [H,I],
+    wu [H,I], wd [I,H] in the logical layout (float32 for the fp32 and fp8
+    recipes -- fp8 weights are quantised on the device by
+    moe_quantize_fp8_blocks -- or bf16 bits); ``layout`` "nk" says they are
+    stored transposed (wg, wu [I,H], wd [H,I]) instead.
     phys_to_logical maps physical ids to entries of ``experts`` (replicas
     share the source but get their own device copy when copy_replicas)."""
 
@@ -65,9 +67,10 @@ class DeviceLayer:
                  shared: Optional[dict] = None,
                  phys_to_logical: Optional[Sequence[int]] = None,
                  l2p=None, replica_count=None, copy_replicas=True,
-                 device="cuda", keep_codes=False):
+                 device="cuda", keep_codes=False, layout="kn"):
         self.p = problem
         self.device = device
+        self.layout = L.LAYOUTS[layout]
         self.keep_codes = keep_codes   # fp8: also keep unpacked codes
         P = problem.num_physical
         if phys_to_logical is None:
@@ -101,28 +104,29 @@ class DeviceLayer:
         out = {}
         for key in ("wg", "wu", "wd"):
             t = to_dev(e[key], self.device)
+            rows, cols = t.shape
+            # reduction size K and outputs N of this matrix
+            K, N = (rows, cols) if self.layout == L.MOE_LAYOUT_KN else (cols, rows)
             if self.fp8:
-                rows, cols = t.shape
                 codes = torch.empty((rows, cols), dtype=torch.uint8,
                                     device=self.device)
-                scales = torch.empty((rows // 128, cols // 128),
+                scales = torch.empty((N // 128, K // 128),
                                      dtype=torch.float32, device=self.device)
-                L.moe_quantize_fp8_blocks(t, rows, cols, 128, codes, scales)
+                L.moe_quantize_fp8_blocks(t, K, N, 128, self.layout, codes,
+                                          scales)
                 packed = torch.empty_like(codes)
-                L.moe_prepack_weights(codes, rows, cols, L.MOE_FP8_E4M3, packed)
+                L.moe_prepack_weights(codes, K, N, L.MOE_FP8_E4M3,
+                                      self.layout, packed)
                 if self.keep_codes:
                     out["codes_" + key] = codes
                 out[key] = packed
                 out["s" + key[1]] = scales
-                del t
-            elif self.p.weight_dtype == L.MOE_BF16:
-                rows, cols = t.shape
-                packed = torch.empty_like(t)
-                L.moe_prepack_weights(t, rows, cols, L.MOE_BF16, packed)
-                out[key] = packed
-                del t
             else:
-                out[key] = t
+                prepared = torch.empty_like(t)
+                L.moe_prepack_weights(t, K, N, self.p.weight_dtype,
+                                      self.layout, prepared)
+                out[key] = prepared
+            del t
         return out
 
     def _tables(self, per_phys, sh) -> L.Weights:

@@ -33,8 +33,10 @@
  *  - Errors are reported only through the returned status; nothing is
  *    printed and nothing aborts.  Argument errors are detected on the host
  *    before any work is enqueued.  Device-data preconditions (finite logits;
- *    map entries in [0, P) or -1; each physical id used by exactly one
- *    (expert, replica)) are not checked.
+ *    topk_ids entries in [0, E); map entries in [0, P) or -1; each physical
+ *    id used by exactly one (expert, replica)) are not checked beyond this:
+ *    an id outside [0, E) is neither counted nor local (its pair_row is -1),
+ *    and a map entry outside [0, P) drops its pair (pair_row -1).
  *  - T = 0 is valid: the call enqueues nothing and succeeds (an idle rank's
  *    dummy forward, infra-guide page, section 4.3).
  *  - Re-entrant; no global mutable state.
@@ -90,17 +92,33 @@ typedef struct {
   int32_t quant_block;  /* fp8 block / group size; must be 128 for FP8      */
 } moe_problem;
 
-/* Expert weights.  w_gate, w_up, w_down (and the scales) are DEVICE arrays of
- * P device pointers, one per physical expert (replicas may alias).  Each
- * matrix is the transpose of the math matrix, i.e. output-major:
- *   gate, up: [I][H]  (row n holds the H weights of output channel n)
- *   down:     [H][I]
- * F32 weights are in this natural row-major layout.  BF16 weights must be in
- * the packed operand layout written by moe_prepack_weights (same bytes,
- * reordered into 16 x 32 blocks).  Element type = weight_dtype.  FP8 weights come with float32 scales, one per
- * 128 x 128 block of the stored matrix: gate/up [I/128][H/128], down
- * [H/128][I/128]; scales are NULL otherwise.  The sh_* members are plain
- * device pointers for the shared expert (NULL when has_shared = 0). */
+/* Storage order of a weight matrix handed to the one-time preparation calls.
+ * An expert is three matrices ("6.4 Data parallelism and expert
+ * parallelism", section 2.1: gate, up, down): W_gate and W_up with H rows and
+ * I columns, W_down with I rows and H columns, so that
+ *   h = silu(x W_gate) * (x W_up)   (x a row of H values)
+ *   y = h W_down.
+ * For a matrix with reduction size K and N output channels (gate/up: K = H,
+ * N = I; down: K = I, N = H):
+ *   MOE_LAYOUT_KN  the logical layout above, row-major [K][N]
+ *   MOE_LAYOUT_NK  its transpose, row-major [N][K] (output-major, the way a
+ *                  linear layer stores its weight) */
+typedef enum { MOE_LAYOUT_KN = 0, MOE_LAYOUT_NK = 1 } moe_layout;
+
+/* Expert weights, in the library's prepared form (made once, off the layer's
+ * path, by moe_prepack_weights from either storage order):
+ *   F32   the logical layout [K][N] itself (W_gate, W_up [H][I]; W_down
+ *         [I][H]); a MOE_LAYOUT_KN source needs no preparation;
+ *   BF16  packed operand blocks (see moe_prepack_weights);
+ *   FP8   packed operand blocks of the E4M3 codes from
+ *         moe_quantize_fp8_blocks, with float32 block scales (one per
+ *         128 x 128 block) in output-block-major order [N/128][K/128]: gate
+ *         and up [I/128][H/128], down [H/128][I/128], whatever the source's
+ *         storage order was; scales are NULL for the other recipes.
+ * w_gate, w_up, w_down and s_gate, s_up, s_down are DEVICE arrays of P
+ * device pointers, one per physical expert (replicas may alias).  The sh_*
+ * members are plain device pointers for the shared expert (NULL when
+ * has_shared = 0).  Element type = weight_dtype. */
 typedef struct {
   const void* const* w_gate;
   const void* const* w_up;
@@ -123,7 +141,11 @@ MOE_API const char* moe_status_string(moe_status s);
 MOE_API moe_status moe_check_problem(const moe_problem* p);
 
 /* Bytes of scratch each entry point needs (host only).  Workspaces must be
- * 256-byte aligned device memory; their contents need not be initialised. */
+ * 256-byte aligned device memory; their contents need not be initialised.
+ * moe_workspace_size gives one size that serves every entry point of the
+ * problem (the largest of the three below); the others give what
+ * moe_dispatch, moe_grouped_ffn and moe_layer_forward need alone. */
+MOE_API moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
 MOE_API moe_status moe_dispatch_workspace_size(const moe_problem* p, size_t* bytes);
 MOE_API moe_status moe_ffn_workspace_size(const moe_problem* p, size_t* bytes);
 MOE_API moe_status moe_layer_workspace_size(const moe_problem* p, size_t* bytes);
@@ -198,6 +220,22 @@ MOE_API moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm,
                            float* y_shared, void* workspace, size_t ws_bytes,
                            void* stream);
 
+/* Where moe_grouped_ffn left the expert intermediate h inside `workspace`
+ * (host only; the workspace passed to that call).  Once the call's work has
+ * completed on its stream, the device arrays hold
+ *   h         [cap + T][I]: routed row r (r < offsets[P], the permuted
+ *             order of moe_dispatch) in row r, the shared expert's row of
+ *             token t in row cap + t; element type bf16 (BF16 recipe), E4M3
+ *             codes (FP8 recipe, the value is code * scale) or float32
+ *   h_scales  [cap + T][I/128] float32 scales of the FP8 recipe (one per row
+ *             per 128 channels), set to NULL for the other recipes
+ * h is the value the down projection multiplies: silu(x W_gate) * (x W_up)
+ * after its rounding (infra-guide page, section 2.1).  WORKSPACE when
+ * ws_bytes is below moe_ffn_workspace_size. */
+MOE_API moe_status moe_ffn_intermediate(const moe_problem* p, void* workspace,
+                                        size_t ws_bytes, void** h,
+                                        float** h_scales);
+
 /* Combine (infra-guide page, section 3.1, step 4: results return to the
  * token and are summed weighted by the route weights).
  *   out[t] = sum over slots j ascending with pair_row[t][j] >= 0 of
@@ -239,31 +277,47 @@ MOE_API moe_status moe_layer_forward_timed(const moe_problem* p,
                                    size_t ws_bytes, void* stream,
                                    void* const* events);
 
-/* One-time weight preparation for the BF16 recipe (not on the layer's path):
- * reorder a natural output-major matrix src [rows][cols] (cols = the
- * reduction: H for gate/up, I for down) into the packed operand layout the
- * expert kernels stream.  The matrix is cut into 16 x 32 blocks; block
- * (r/16, c/32) is stored at block index (r/16) * (cols/32) + c/32, 1 KiB per
- * block; inside a block, 16-byte lane L = r%16 + 16 * ((c%32) / 8) holds the
- * 8 consecutive elements with c%8 = 0..7.  16 output channels over the whole
- * reduction thus form one contiguous run, and each 1 KiB block is one
- * wavefront's matrix-core operand.  dtype must be MOE_BF16; rows % 16 == 0,
- * cols % 32 == 0; src and dst are distinct device buffers of rows*cols
- * elements. */
-MOE_API moe_status moe_prepack_weights(const void* src, int32_t rows,
-                                       int32_t cols, int32_t dtype, void* dst,
-                                       void* stream);
+/* One-time weight preparation (not on the layer's path): a matrix with
+ * reduction size K and N output channels, stored as `layout` says (see
+ * moe_layout: gate/up K = H, N = I; down K = I, N = H), into the prepared
+ * form that moe_weights holds for `dtype`:
+ *   MOE_F32       dst = the logical layout [K][N] (a copy, or the transpose
+ *                 of a MOE_LAYOUT_NK source)
+ *   MOE_BF16      packed operand blocks: the matrix is cut into blocks of 16
+ *                 output channels x 32 reduction values; block (n/16, k/32)
+ *                 is stored at block index (n/16) * (K/32) + k/32, 1 KiB per
+ *                 block; inside a block, 16-byte lane L = n%16 + 16*((k%32)/8)
+ *                 holds the 8 values k%8 = 0..7.  16 output channels over the
+ *                 whole reduction form one contiguous run and each 1 KiB block
+ *                 is one wavefront's matrix-core operand.  Needs N % 16 == 0,
+ *                 K % 32 == 0.
+ *   MOE_FP8_E4M3  src holds E4M3 codes (from moe_quantize_fp8_blocks);
+ *                 blocks of 16 output channels x 128 reduction values, 2 KiB,
+ *                 block (n/16, k/128) at block index (n/16) * (K/128) + k/128;
+ *                 lane L = n%16 + 16*((k%128)/32) owns 32 codes, the first 16
+ *                 at byte L*16 of the block and the rest at 1024 + L*16.
+ *                 Needs N % 16 == 0, K % 128 == 0.
+ * src and dst are distinct device buffers of K*N elements.  UNSUPPORTED for
+ * another dtype, INVALID_ARGUMENT for a bad layout or shape. */
+MOE_API moe_status moe_prepack_weights(const void* src, int32_t K, int32_t N,
+                                       int32_t dtype, int32_t layout,
+                                       void* dst, void* stream);
 
 /* One-time weight preparation for the FP8 recipe (not on the layer's path):
- * quantise a float32 matrix [rows][cols] to E4M3 with one float32 scale per
- * block x block tile (scale = amax/448, 1 for an all-zero tile; code = RNE of
- * fl32(w/scale), saturated to +-448).  rows and cols must be multiples of
- * block (= 128).
- *   w [rows][cols] float32; codes [rows][cols] uint8 out;
- *   scales [rows/block][cols/block] float32 out. */
-MOE_API moe_status moe_quantize_fp8_blocks(const float* w, int32_t rows, int32_t cols,
-                                   int32_t block, uint8_t* codes,
-                                   float* scales, void* stream);
+ * quantise a float32 matrix (reduction size K, N outputs, stored as `layout`
+ * says) to E4M3 with one float32 scale per block x block tile (block = 128):
+ * scale = amax/448 over the tile (1 for an all-zero tile), code = RNE of
+ * fl32(w/scale) saturated to +-448.
+ *   w      float32 [K][N] (MOE_LAYOUT_KN) or [N][K] (MOE_LAYOUT_NK)
+ *   codes  uint8 out, in the same storage order as w (to be packed by
+ *          moe_prepack_weights with the same layout)
+ *   scales float32 out, [N/128][K/128] whatever the layout (the order
+ *          moe_weights takes).
+ * K and N must be multiples of block. */
+MOE_API moe_status moe_quantize_fp8_blocks(const float* w, int32_t K, int32_t N,
+                                   int32_t block, int32_t layout,
+                                   uint8_t* codes, float* scales,
+                                   void* stream);
 
 /* Host-side replica map for a skewed rank (infra-guide page, section 5.3:
  * redundant experts replicate hot experts so their load splits).  The

@@ -115,3 +115,56 @@ def dequantize_rows(codes: np.ndarray, scales: np.ndarray,
     N, K = codes.shape
     v = e4m3_decode(codes).reshape(N, K // group, group)
     return (v * scales.astype(np.float64)[:, :, None]).reshape(N, K)
+
+
+# ------------------------------------- codes a float32 evaluation may give
+def row_scale_interval(h64: np.ndarray, eps: np.ndarray, group: int = 128):
+    """Range of the per-row, per-``group`` scale fl32(amax/448) when each
+    element of h may be off by up to ``eps`` (float64 arrays [N, K]): amax
+    lies between max(|h| - eps, 0) and max(|h| + eps) over the group, and
+    rounding to float32 and the division are monotone.  Returns float32
+    (s_lo, s_hi), each [N, K/group]."""
+    N, K = h64.shape
+    a = np.abs(h64).reshape(N, K // group, group)
+    e = np.asarray(eps, dtype=np.float64).reshape(N, K // group, group)
+    lo = np.maximum(a - e, 0.0).max(axis=2)
+    hi = (a + e).max(axis=2)
+    # amax is itself a float32 value inside [lo, hi]
+    lo32 = _round_f32_down(lo)
+    hi32 = _round_f32_up(hi)
+    return _scale_from_amax(lo32), _scale_from_amax(hi32)
+
+
+def row_code_interval(h64: np.ndarray, eps: np.ndarray, s_lo: np.ndarray,
+                      s_hi: np.ndarray, group: int = 128):
+    """Smallest and largest E4M3 value that round-to-nearest-even of
+    fl32(v / s) can give for some v in [h - eps, h + eps] and some scale s in
+    [s_lo, s_hi] (float32 [N, K/group]).  Division, rounding to float32 and
+    the saturating E4M3 rounding are all monotone, so the ends of the
+    quotient interval give the ends of the code interval.  Returns float64
+    arrays (vmin, vmax) [N, K] of code values (not multiplied by the
+    scale)."""
+    slo = np.repeat(np.asarray(s_lo, dtype=np.float64), group, axis=1)
+    shi = np.repeat(np.asarray(s_hi, dtype=np.float64), group, axis=1)
+    e = np.asarray(eps, dtype=np.float64)
+    a, b = h64 - e, h64 + e
+    qlo = np.where(a >= 0, a / shi, a / slo)          # min of a / s
+    qhi = np.where(b >= 0, b / slo, b / shi)          # max of b / s
+    # the float64 quotients are widened past their own rounding
+    qlo = qlo - np.abs(qlo) * 2.0 ** -50
+    qhi = qhi + np.abs(qhi) * 2.0 ** -50
+    lo = e4m3_decode(e4m3_encode(qlo.astype(np.float32)))
+    hi = e4m3_decode(e4m3_encode(qhi.astype(np.float32)))
+    return lo, hi
+
+
+def _round_f32_down(v: np.ndarray) -> np.ndarray:
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    return np.where(f.astype(np.float64) > v, np.nextafter(f, np.float32(-np.inf)),
+                    f).astype(np.float32)
+
+
+def _round_f32_up(v: np.ndarray) -> np.ndarray:
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    return np.where(f.astype(np.float64) < v, np.nextafter(f, np.float32(np.inf)),
+                    f).astype(np.float32)

@@ -179,12 +179,78 @@ def silu(z: np.ndarray) -> np.ndarray:
 def swiglu(x64: np.ndarray, wg64: np.ndarray, wu64: np.ndarray,
            wd64: np.ndarray, h_round) -> np.ndarray:
     """One expert on the rows of x64 [n, H]: y = round(silu(x Wg) * (x Wu)) Wd,
-    with Wg, Wu given as stored [I, H] and Wd as stored [H, I] (transposes of
-    the H x I and I x H matrices)."""
-    g = x64 @ wg64.T
-    u = x64 @ wu64.T
+    with Wg, Wu the H x I matrices and Wd the I x H matrix."""
+    g = x64 @ wg64
+    u = x64 @ wu64
     h = h_round(silu(g) * u)
-    return h @ wd64.T
+    return h @ wd64
+
+
+# ---------------------------- what a float32 evaluation of h may differ by
+U32 = 2.0 ** -24           # unit roundoff of float32
+LAMBDA = 8.0               # scales of the accumulation error the bound allows
+
+
+def h_eval_bound(x64: np.ndarray, wg64: np.ndarray, wu64: np.ndarray,
+                 g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Bound on |h_fl32 - h| for h = silu(x Wg) * (x Wu) evaluated in float32.
+
+    Accumulation: g (and u) is a sum of K products p_k = x_k w_k.  Summed in
+    float32 in any fixed order (a matrix core's blocks included; the FP8
+    recipe's two per-block scale multiplies count as two more steps), the
+    error to first order is sum_i d_i S_i over the K + 2 operations, with
+    |d_i| <= u = 2^-24 independent and mean-zero for round-to-nearest, and
+    S_i the partial sums.  For the synthetic inputs the products are
+    independent zero-mean draws, so in any order that does not look at the
+    data the partial sums grow like a random walk, sum_i S_i^2 ~ (K^2 / 2)
+    mean(p^2) = (K / 2) ||p||^2, and the error is sub-Gaussian with scale
+    u sqrt(K / 2) ||p||.  The bound takes LAMBDA = 8 of those scales.
+    silu(z) = z / (1 + exp(-z)): |silu'| <= 1.1, and its float32 evaluation
+    (the exponent's argument rounded, exp to within 2 ulp, one add, one
+    divide) has relative error below (|z| + 6) u; the bound takes twice that.
+    The product silu(g) * u adds one rounding."""
+    K = x64.shape[1]
+    scale = LAMBDA * U32 * np.sqrt((K + 2.0) / 2.0)
+    x2 = x64 * x64
+    eg = scale * np.sqrt(x2 @ (wg64 * wg64))
+    eu = scale * np.sqrt(x2 @ (wu64 * wu64))
+    sg = silu(g)
+    es = 1.1 * eg + 2.0 * (np.abs(g) + 6.0) * U32 * np.abs(sg)
+    h = sg * u
+    return np.abs(u) * es + np.abs(sg) * eu + es * eu + U32 * np.abs(h)
+
+
+@dataclasses.dataclass
+class Fp8Rows:
+    """Per routed (or shared) row of the FP8 recipe: the exact h, the
+    interval of scales and E4M3 code values a correct float32 evaluation may
+    produce for it (a value near a rounding boundary has two correct codes),
+    and the largest change of the dequantised h that choice allows."""
+    h: np.ndarray            # [n, I] float64, exact silu(x Wg) * (x Wu)
+    s_lo: np.ndarray         # [n, I/128] float32
+    s_hi: np.ndarray
+    v_lo: np.ndarray         # [n, I] float64 code values
+    v_hi: np.ndarray
+    allow: np.ndarray        # [n, I] max |dequantised h - oracle's own|
+
+
+def fp8_rows_detail(x64, wg64, wu64, block: int = 128):
+    """h, its code and scale intervals, and the oracle's own rounding of it
+    (for ``Fp8Rows`` and the down projection)."""
+    g = x64 @ wg64
+    u = x64 @ wu64
+    h = silu(g) * u
+    eps = h_eval_bound(x64, wg64, wu64, g, u)
+    s_lo, s_hi = _fp8.row_scale_interval(h, eps, block)
+    v_lo, v_hi = _fp8.row_code_interval(h, eps, s_lo, s_hi, block)
+    slo = np.repeat(s_lo.astype(np.float64), block, axis=1)
+    shi = np.repeat(s_hi.astype(np.float64), block, axis=1)
+    d_lo = np.minimum(v_lo * slo, v_lo * shi)
+    d_hi = np.maximum(v_hi * slo, v_hi * shi)
+    own = h_rounder("fp8", "bf16", block)(h)
+    allow = np.maximum(d_hi - own, own - d_lo)
+    return Fp8Rows(h=h, s_lo=s_lo, s_hi=s_hi, v_lo=v_lo, v_hi=v_hi,
+                   allow=allow), own
 
 
 @dataclasses.dataclass
@@ -201,6 +267,9 @@ class ExpertSet:
     quant_block: int = 128
     loader: Optional[object] = None
     shared_loader: Optional[object] = None
+    # the workload the weights come from (a copy without cached tensors), so
+    # worker threads can make an expert's weights themselves
+    source: Optional[object] = None
 
     def get(self, e: int) -> tuple:
         if self.experts is not None:
@@ -232,16 +301,18 @@ def expert_set_from_workload(w, experts: Optional[Sequence[int]] = None,
         d = w.shared_expert
         return conv(d["wg"]), conv(d["wu"]), conv(d["wd"])
 
+    source = dataclasses.replace(w, _experts={}, _cache={})
     if lazy:
         return ExpertSet(fmt=w.wdt, quant_block=w.quant_block, loader=load,
-                         shared_loader=load_shared if w.shared else None)
+                         shared_loader=load_shared if w.shared else None,
+                         source=source)
     idx = range(w.num_local) if experts is None else experts
     ex = [None] * w.num_local
     for e in idx:
         ex[e] = load(e)
     sh = load_shared() if w.shared else None
     return ExpertSet(fmt=w.wdt, experts=ex, shared=sh,
-                     quant_block=w.quant_block)
+                     quant_block=w.quant_block, source=source)
 
 
 def _weight_converter(wdt: str, block: int):
@@ -303,17 +374,77 @@ class LayerResult:
     y_rows: np.ndarray
     shared_out: Optional[np.ndarray]
     out: np.ndarray
+    # FP8 recipe with fp8_detail: per routed row (permuted order) and per
+    # shared row, the h intervals; out_allow [T, H] bounds how far a correct
+    # choice among the alternative h codes moves each output element
+    fp8_routed: Optional[Fp8Rows] = None
+    fp8_shared: Optional[Fp8Rows] = None
+    out_allow: Optional[np.ndarray] = None
+
+
+def _eval_expert(weights, xrs, fmt: str, act: str, block: int,
+                 detail: bool):
+    """One expert on each of the row sets ``xrs``: per set (y, allowance or
+    None, Fp8Rows or None)."""
+    wg, wu, wd = weights
+    out = []
+    for xr in xrs:
+        if detail:
+            det, hq = fp8_rows_detail(xr, wg, wu, block)
+            out.append((hq @ wd, det.allow @ np.abs(wd), det))
+        else:
+            out.append((swiglu(xr, wg, wu, wd, h_rounder(fmt, act, block)),
+                        None, None))
+    return out
+
+
+def _expert_job(source, e: int, xrs, act: str, detail: bool):
+    """One expert's evaluation from the workload alone: its weights are made
+    from the workload's generator (expert -1 is the shared one)."""
+    conv = _weight_converter(source.wdt, source.quant_block)
+    d = source.expert(e) if e >= 0 else source.shared_expert
+    weights = (conv(d["wg"]), conv(d["wu"]), conv(d["wd"]))
+    return _eval_expert(weights, xrs, source.wdt, act, source.quant_block,
+                        detail)
+
+
+def _run_experts(jobs, experts: "ExpertSet", act: str, detail: bool,
+                 workers: int):
+    """Evaluate (expert, row sets) jobs in order; with ``workers`` > 1 and a
+    workload behind the expert set, on that many threads (NumPy releases the
+    interpreter lock in its array loops; the same arithmetic, one expert per
+    thread at a time)."""
+    if workers > 1 and experts.source is not None and len(jobs) > 1:
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(max_workers=min(workers, len(jobs))) as pool:
+            futs = [pool.submit(_expert_job, experts.source, e, xrs, act,
+                                detail) for e, _, xrs in jobs]
+            for (e, parts, _), f in zip(jobs, futs):
+                yield e, parts, f.result()
+        return
+    for e, parts, xrs in jobs:
+        weights = experts.get(e) if e >= 0 else experts.get_shared()
+        res = _eval_expert(weights, xrs, experts.fmt, act,
+                           experts.quant_block, detail)
+        del weights
+        yield e, parts, res
 
 
 def layer_forward(logits, bias, x_stored, act: str, k: int, expert_begin: int,
                   num_local: int, experts: ExpertSet, l2p=None, rep_count=None,
-                  P: Optional[int] = None, token_subset=None) -> LayerResult:
+                  P: Optional[int] = None, token_subset=None,
+                  fp8_detail: bool = False, workers: int = 0) -> LayerResult:
     """The whole layer: route -> dispatch -> experts -> combine.
 
     ``experts.experts[e]`` are the weights of local logical expert e; all
     replicas of e compute with the same weights.  ``token_subset`` (optional)
     restricts the expert evaluation and the output to those tokens, for
-    spot checks of large workloads (routing and dispatch still cover all)."""
+    spot checks of large workloads (routing and dispatch still cover all).
+    ``fp8_detail`` (FP8 recipe) also records, for every evaluated row, the
+    codes and scales a correct float32 evaluation of h may give
+    (``fp8_rows_detail``) and the resulting allowance on the output.
+    ``workers`` > 1 evaluates the experts on that many threads (expert sets
+    made by ``expert_set_from_workload`` only)."""
     ids, w, counts = route_topk(logits, k, bias)
     if l2p is None:
         l2p, rep_count = identity_map(num_local)
@@ -333,7 +464,10 @@ def layer_forward(logits, bias, x_stored, act: str, k: int, expert_begin: int,
     if token_subset is not None:
         want = np.zeros(T, dtype=bool)
         want[np.asarray(token_subset)] = True
+    detail = fp8_detail and experts.fmt == "fp8"
     y_rows = np.zeros((d.N, H), dtype=np.float64)
+    y_allow = np.zeros((d.N, H), dtype=np.float64) if detail else None
+    rows_detail = {}
     by_expert = {}
     for p in range(P):
         lo, hi = int(d.offsets[p]), int(d.offsets[p + 1])
@@ -344,31 +478,69 @@ def layer_forward(logits, bias, x_stored, act: str, k: int, expert_begin: int,
         if rows.size == 0:
             continue
         by_expert.setdefault(int(phys_to_logical[p]), []).append(rows)
-    for e, parts in sorted(by_expert.items()):
-        wg, wu, wd = experts.get(e)
-        for rows in parts:
-            y_rows[rows] = swiglu(x_rows[d.row_token[rows]], wg, wu, wd, hr)
-        del wg, wu, wd
-    shared_out = None
+    # every logical expert's rows (and the shared expert's, as expert -1)
+    jobs = [(e, parts, [x_rows[d.row_token[r]] for r in parts])
+            for e, parts in sorted(by_expert.items())]
     if experts.has_shared:
-        shared_out = np.zeros((T, H), dtype=np.float64)
-        wg, wu, wd = experts.get_shared()
-        shared_out[want] = swiglu(x_rows[want], wg, wu, wd, hr)
+        jobs.append((-1, [np.flatnonzero(want)], [x_rows[want]]))
+    shared_out = shared_det = shared_allow = None
+    for e, parts, results in _run_experts(jobs, experts, act, detail,
+                                          workers):
+        if e < 0:
+            shared_out = np.zeros((T, H), dtype=np.float64)
+            y, allow, shared_det = results[0]
+            shared_out[want] = y
+            if detail:
+                shared_allow = np.zeros((T, H), dtype=np.float64)
+                shared_allow[want] = allow
+            continue
+        for rows, (y, allow, det) in zip(parts, results):
+            y_rows[rows] = y
+            if detail:
+                y_allow[rows] = allow
+                rows_detail[tuple(rows[[0, -1]])] = (rows, det)
     pr = d.pair_row.copy()
     pr[~want] = -1
     out = combine(y_rows, pr, w, shared_out, T, H)
-    return LayerResult(ids=ids, weights=w, counts=counts, disp=d,
-                       y_rows=y_rows, shared_out=shared_out, out=out)
+    res = LayerResult(ids=ids, weights=w, counts=counts, disp=d,
+                      y_rows=y_rows, shared_out=shared_out, out=out)
+    if detail:
+        # the allowance adds up like the output: |w| times each row's own
+        res.out_allow = combine(y_allow, pr, np.abs(w), shared_allow, T, H)
+        res.fp8_routed = _gather_rows_detail(rows_detail, d.N)
+        res.fp8_shared = shared_det
+    return res
+
+
+def _gather_rows_detail(parts: dict, n_rows: int) -> Fp8Rows:
+    """Per-expert pieces of ``Fp8Rows`` placed at their permuted rows (rows
+    that were not evaluated stay NaN)."""
+    first = next(iter(parts.values()))[1] if parts else None
+    if first is None:
+        return None
+    I_ = first.h.shape[1]
+    G = first.s_lo.shape[1]
+    out = Fp8Rows(h=np.full((n_rows, I_), np.nan),
+                  s_lo=np.full((n_rows, G), np.nan, dtype=np.float32),
+                  s_hi=np.full((n_rows, G), np.nan, dtype=np.float32),
+                  v_lo=np.full((n_rows, I_), np.nan),
+                  v_hi=np.full((n_rows, I_), np.nan),
+                  allow=np.full((n_rows, I_), np.nan))
+    for rows, det in parts.values():
+        for f in ("h", "s_lo", "s_hi", "v_lo", "v_hi", "allow"):
+            getattr(out, f)[rows] = getattr(det, f)
+    return out
 
 
 def layer_from_workload(wl, experts: Optional[ExpertSet] = None,
                         l2p=None, rep_count=None, P=None,
-                        token_subset=None) -> LayerResult:
+                        token_subset=None, fp8_detail=False,
+                        workers: int = 0) -> LayerResult:
     if experts is None:
-        experts = expert_set_from_workload(wl)
+        experts = expert_set_from_workload(wl, lazy=workers > 1)
     return layer_forward(wl.logits, wl.bias, wl.x, wl.act, wl.k,
                          wl.expert_begin, wl.num_local, experts, l2p,
-                         rep_count, P, token_subset)
+                         rep_count, P, token_subset, fp8_detail, workers)
 
 
 # ------------------------------------------------------ dense brute force

@@ -26,9 +26,9 @@ always-on shared expert, one EP rank's contiguous share of experts):
 Stored layouts (row-major):
 * ``logits`` [T, E] float32, ``bias`` [E] float32 or None;
 * ``x`` [T, H]: float32 for fp32 workloads, else bf16 bit patterns (uint16);
-* per expert ``wg``, ``wu`` [I, H] and ``wd`` [H, I]: the transposes of the
-  H x I gate/up and I x H down matrices (output-major, like a linear layer's
-  weight), float32 or bf16 bit patterns.
+* per expert ``wg``, ``wu`` [H, I] and ``wd`` [I, H]: the gate/up and down
+  matrices in their logical layout (h = silu(x Wg) * (x Wu), y = h Wd), float32
+  or bf16 bit patterns.
 
 Normals are drawn in float32 with numpy's PCG64 generator seeded by
 ``[seed, workload id, tensor id, index]``, then rounded to nearest-even bf16
@@ -156,14 +156,14 @@ class Workload:
     def _weights(self, tensor: int, index: int) -> dict:
         rng = self._rng(tensor, index)
         fmt = "bf16" if self.wdt == "bf16" else "f32"
-        wg = self._store(self._normal(rng, (self.I, self.H), WEIGHT_STD), fmt)
-        wu = self._store(self._normal(rng, (self.I, self.H), WEIGHT_STD), fmt)
-        wd = self._store(self._normal(rng, (self.H, self.I), WEIGHT_STD), fmt)
+        wg = self._store(self._normal(rng, (self.H, self.I), WEIGHT_STD), fmt)
+        wu = self._store(self._normal(rng, (self.H, self.I), WEIGHT_STD), fmt)
+        wd = self._store(self._normal(rng, (self.I, self.H), WEIGHT_STD), fmt)
         return dict(wg=wg, wu=wu, wd=wd)
 
     def expert(self, e_local: int) -> dict:
         """Weights of local logical expert ``e_local`` (global id
-        expert_begin + e_local): dict(wg [I,H], wu [I,H], wd [H,I])."""
+        expert_begin + e_local): dict(wg [H,I], wu [H,I], wd [I,H])."""
         if not 0 <= e_local < self.num_local:
             raise IndexError(e_local)
         if e_local not in self._experts:

@@ -144,14 +144,18 @@ def test_weights_struct_is_checked():
 
 
 def test_fp8_quantiser_checks_shapes():
-    st = m.moe_quantize_fp8_blocks(256, 100, 128, 128, 256, 256, stream=0,
+    KN = L.MOE_LAYOUT_KN
+    st = m.moe_quantize_fp8_blocks(256, 100, 128, 128, KN, 256, 256, stream=0,
                                    check=False)
     assert st == L.MOE_ERR_INVALID_ARGUMENT
-    st = m.moe_quantize_fp8_blocks(256, 128, 128, 64, 256, 256, stream=0,
+    st = m.moe_quantize_fp8_blocks(256, 128, 128, 64, KN, 256, 256, stream=0,
                                    check=False)
     assert st == L.MOE_ERR_UNSUPPORTED
-    assert m.moe_quantize_fp8_blocks(None, 0, 0, 128, None, None, stream=0,
-                                     check=False) == L.MOE_OK
+    st = m.moe_quantize_fp8_blocks(256, 128, 128, 128, 2, 256, 256, stream=0,
+                                   check=False)
+    assert st == L.MOE_ERR_INVALID_ARGUMENT          # no such layout
+    assert m.moe_quantize_fp8_blocks(None, 0, 0, 128, KN, None, None,
+                                     stream=0, check=False) == L.MOE_OK
 
 
 @pytest.mark.parametrize("counts,red", [
@@ -172,18 +176,53 @@ def test_hottest_map_rejects_bad_arguments():
 
 
 def test_prepack_checks_arguments():
-    assert m.moe_prepack_weights(256, 16, 30, L.MOE_BF16, 512, stream=0,
+    KN, NK = L.MOE_LAYOUT_KN, L.MOE_LAYOUT_NK
+    # bf16: K (the reduction) a multiple of 32, N a multiple of 16
+    assert m.moe_prepack_weights(256, 30, 16, L.MOE_BF16, KN, 512, stream=0,
                                  check=False) == L.MOE_ERR_INVALID_ARGUMENT
-    assert m.moe_prepack_weights(256, 16, 32, L.MOE_F32, 512, stream=0,
+    assert m.moe_prepack_weights(256, 32, 24, L.MOE_BF16, NK, 512, stream=0,
+                                 check=False) == L.MOE_ERR_INVALID_ARGUMENT
+    assert m.moe_prepack_weights(256, 32, 16, 7, KN, 512, stream=0,
                                  check=False) == L.MOE_ERR_UNSUPPORTED
-    assert m.moe_prepack_weights(256, 16, 32, L.MOE_BF16, 256, stream=0,
+    assert m.moe_prepack_weights(256, 32, 16, L.MOE_BF16, 5, 512, stream=0,
                                  check=False) == L.MOE_ERR_INVALID_ARGUMENT
-    assert m.moe_prepack_weights(None, 0, 32, L.MOE_BF16, None, stream=0,
+    assert m.moe_prepack_weights(256, 32, 16, L.MOE_BF16, KN, 256, stream=0,
+                                 check=False) == L.MOE_ERR_INVALID_ARGUMENT
+    assert m.moe_prepack_weights(None, 32, 0, L.MOE_BF16, KN, None, stream=0,
                                  check=False) == L.MOE_OK
 
 
 def test_prepack_fp8_checks_arguments():
-    assert m.moe_prepack_weights(256, 16, 64, L.MOE_FP8_E4M3, 512, stream=0,
-                                 check=False) == L.MOE_ERR_INVALID_ARGUMENT
-    assert m.moe_prepack_weights(256, 8, 128, L.MOE_FP8_E4M3, 512, stream=0,
-                                 check=False) == L.MOE_ERR_INVALID_ARGUMENT
+    KN = L.MOE_LAYOUT_KN
+    assert m.moe_prepack_weights(256, 64, 16, L.MOE_FP8_E4M3, KN, 512,
+                                 stream=0, check=False) == \
+        L.MOE_ERR_INVALID_ARGUMENT
+    assert m.moe_prepack_weights(256, 128, 8, L.MOE_FP8_E4M3, KN, 512,
+                                 stream=0, check=False) == \
+        L.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_one_workspace_serves_every_entry_point():
+    for p in (good(), good(has_shared=True), good(wdt="fp8"),
+              good(T=3000, num_physical=12, max_replicas=2)):
+        total = m.moe_workspace_size(p)
+        assert total == max(m.moe_dispatch_workspace_size(p),
+                            m.moe_ffn_workspace_size(p),
+                            m.moe_layer_workspace_size(p))
+
+
+def test_intermediate_lies_inside_the_ffn_workspace():
+    for p, hb in ((good(), 2), (good(wdt="fp8"), 1),
+                  (good(act="f32", wdt="f32", out="f32"), 4)):
+        need = m.moe_ffn_workspace_size(p)
+        base = 1 << 20
+        h, hs = m.moe_ffn_intermediate(p, base, need)
+        cap = p.T * min(p.k, p.num_local)
+        assert base <= h and h + cap * p.I * hb <= base + need
+        if p.weight_dtype == L.MOE_FP8_E4M3:
+            assert hs is not None and h < hs
+            assert hs + cap * (p.I // 128) * 4 <= base + need
+        else:
+            assert hs is None
+    with pytest.raises(m.MoeError):
+        m.moe_ffn_intermediate(good(), 1 << 20, 16)

@@ -16,11 +16,12 @@ from .helpers import (BARS, check_output, device_layer, out_to_f64,
 pytestmark = pytest.mark.gpu
 
 
-def run_layer(wl, l2p=None, rep=None, P=None, steps=False):
+def run_layer(wl, l2p=None, rep=None, P=None, steps=False, layout="kn"):
     import torch
     from expert_moe_fp32_amd.runner import to_dev
     ptl = None if l2p is None else phys_to_logical_from_map(l2p, rep, P)
-    dl = device_layer(wl, l2p=l2p, rep=rep, P=P, phys_to_logical=ptl)
+    dl = device_layer(wl, l2p=l2p, rep=rep, P=P, phys_to_logical=ptl,
+                      layout=layout)
     b = dl.buffers()
     dlog = to_dev(wl.logits)
     dbias = None if wl.bias is None else to_dev(wl.bias)
@@ -40,10 +41,10 @@ def run_layer(wl, l2p=None, rep=None, P=None, steps=False):
     return out, counts
 
 
-def oracle_out(wl, tokens=None, l2p=None, rep=None, P=None):
+def oracle_out(wl, tokens=None, l2p=None, rep=None, P=None, workers=0):
     ex = omoe.expert_set_from_workload(wl, lazy=True)
     res = omoe.layer_from_workload(wl, ex, l2p=l2p, rep_count=rep, P=P,
-                                   token_subset=tokens)
+                                   token_subset=tokens, workers=workers)
     return res
 
 
@@ -86,6 +87,25 @@ def test_layer_reduced_shapes(name, kw):
     print(f"  max|err|/RMS = {r:.3e}")
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", dict(T=100, E=16, num_local=8, k=2)),                  # fp32
+    ("decode", dict(T=64, H=384, I=256, E=32, num_local=8, k=4)),   # stream
+    ("prefill", dict(T=300, H=256, I=256, E=16, num_local=8, k=4)),  # ring
+])
+def test_weights_in_either_storage_order(name, kw):
+    """The expert matrices handed over in their logical layout (W_gate,
+    W_up [H][I], W_down [I][H]; "6.4 Data parallelism and expert
+    parallelism", section 2.1) -- the layout every other test uses -- or
+    transposed (output-major) give bit-identical layers, both matching the
+    oracle."""
+    wl = make_workload(name, seed=14, **kw)
+    a, _ = run_layer(wl, layout="kn")
+    b, _ = run_layer(wl, layout="nk")
+    assert np.array_equal(a, b)
+    check_output(a, oracle_out(wl).out, wl.out, BARS[recipe(wl)],
+                 wl.describe())
+
+
 def test_steps_equal_layer_forward():
     wl = make_workload("prefill", seed=12, T=200, H=256, I=128, E=16,
                        num_local=8, k=4)
@@ -105,12 +125,17 @@ def test_tokens_without_local_pairs_get_zero_rows():
     check_output(out, ref.out, wl.out, BARS["bf16"])
 
 
-def test_full_decode_all_tokens():
-    wl = make_workload("decode", seed=0)
+@pytest.mark.parametrize("out_fmt", ["bf16", "f32"])
+def test_full_decode_all_tokens(out_fmt):
+    """The decode workload at full size, every token.  With float32 output
+    the bar applies to the raw error (no allowance for any rounding of the
+    output); with bf16 output beyond the output's own rounding."""
+    wl = make_workload("decode", seed=0, out=out_fmt)
     print(f"layer {wl.describe()}", flush=True)
     out, _ = run_layer(wl)
-    ref = oracle_out(wl)
-    r = check_output(out, ref.out, wl.out, BARS["bf16"], "decode")
+    ref = oracle_out(wl, workers=16)
+    r = check_output(out, ref.out, wl.out, BARS["bf16"], "decode",
+                     literal=out_fmt == "f32")
     print(f"  max|err|/RMS = {r:.3e}")
 
 
@@ -119,13 +144,18 @@ def skewed():
     return make_workload("skewed", seed=0)
 
 
-def test_full_prefill_sampled():
-    wl = make_workload("prefill", seed=0)
+@pytest.mark.parametrize("out_fmt", ["bf16", "f32"])
+def test_full_prefill_sampled(out_fmt):
+    """The prefill workload at full size (T = 8192, shared expert) on 256
+    sampled tokens (the oracle evaluates every expert on their rows); with
+    float32 output against the raw bar."""
+    wl = make_workload("prefill", seed=0, out=out_fmt)
     print(f"layer {wl.describe()}", flush=True)
     out, _ = run_layer(wl)
-    tok = sample_tokens(wl.T, 20)
-    ref = oracle_out(wl, tokens=tok)
-    r = check_output(out[tok], ref.out[tok], wl.out, BARS["bf16"], "prefill")
+    tok = sample_tokens(wl.T, 256)
+    ref = oracle_out(wl, tokens=tok, workers=16)
+    r = check_output(out[tok], ref.out[tok], wl.out, BARS["bf16"], "prefill",
+                     literal=out_fmt == "f32")
     print(f"  max|err|/RMS = {r:.3e}")
 
 
@@ -138,8 +168,8 @@ def test_full_skewed_with_and_without_replicas(skewed):
     out_b, _ = run_layer(wl, l2p=l2p, rep=rep, P=P)
     # replicas compute with the same weights in the same order
     assert np.array_equal(out_a, out_b)
-    tok = sample_tokens(wl.T, 16, seed=1)
-    ref = oracle_out(wl, tokens=tok, l2p=l2p, rep=rep, P=P)
+    tok = sample_tokens(wl.T, 256, seed=1)
+    ref = oracle_out(wl, tokens=tok, l2p=l2p, rep=rep, P=P, workers=16)
     check_output(out_b[tok], ref.out[tok], wl.out, BARS["bf16"], "skewed")
     base = ref.disp.logical_counts
     print(f"  busiest/mean local expert: a {base.max() / base.mean():.2f}, "

@@ -107,3 +107,117 @@ def test_row_quantiser_groups():
     assert np.all(np.abs(deq - a) <= np.repeat(s, 128, 1) * 16 + 1e-12)
     with pytest.raises(ValueError):
         fp8.quantize_rows(a[:, :100], 128)
+
+
+# ------------------------------------ codes a float32 evaluation may give
+def test_intervals_collapse_without_error():
+    """With eps = 0 the scale and code intervals are the quantiser's own
+    scale and code."""
+    rng = np.random.default_rng(11)
+    h = rng.standard_normal((6, 256)) * 0.3
+    codes, s = fp8.quantize_rows(h.astype(np.float32), 128)
+    h32 = h.astype(np.float32).astype(np.float64)
+    z = np.zeros_like(h32)
+    s_lo, s_hi = fp8.row_scale_interval(h32, z)
+    assert np.array_equal(s_lo, s) and np.array_equal(s_hi, s)
+    v_lo, v_hi = fp8.row_code_interval(h32, z, s_lo, s_hi)
+    assert np.array_equal(v_lo, fp8.e4m3_decode(codes))
+    assert np.array_equal(v_hi, fp8.e4m3_decode(codes))
+
+
+def test_a_value_at_a_rounding_boundary_has_two_codes():
+    """Hand-worked: with scale 1 (group maximum 448), 1.0625 lies half way
+    between the E4M3 values 1.0 and 1.125; any error window around it admits
+    both, while 1.03 (a quarter step from 1.0) keeps one code for a window
+    of 0.01."""
+    h = np.zeros((1, 128))
+    h[0, 0] = 448.0
+    h[0, 1] = 1.0625
+    h[0, 2] = 1.03
+    eps = np.zeros_like(h)
+    eps[0, 1:3] = 0.01
+    s_lo, s_hi = fp8.row_scale_interval(h, eps)
+    assert s_lo[0, 0] == s_hi[0, 0] == np.float32(1.0)
+    v_lo, v_hi = fp8.row_code_interval(h, eps, s_lo, s_hi)
+    assert (v_lo[0, 1], v_hi[0, 1]) == (1.0, 1.125)
+    assert (v_lo[0, 2], v_hi[0, 2]) == (1.0, 1.0)
+    assert (v_lo[0, 0], v_hi[0, 0]) == (448.0, 448.0)
+
+
+def test_perturbed_quantisations_stay_inside_the_intervals():
+    """Brute force: many float32 perturbations of h, each no larger than
+    eps, quantised by the oracle's own row quantiser, give scales and codes
+    inside the intervals."""
+    rng = np.random.default_rng(12)
+    h = rng.standard_normal((8, 384))
+    eps = np.abs(h) * 1e-3 + 1e-6
+    s_lo, s_hi = fp8.row_scale_interval(h, eps)
+    v_lo, v_hi = fp8.row_code_interval(h, eps, s_lo, s_hi)
+    wide = 0
+    for trial in range(40):
+        hp = h + eps * rng.uniform(-1.0, 1.0, size=h.shape)
+        if trial == 0:
+            hp = h + eps                       # the window's ends
+        elif trial == 1:
+            hp = h - eps
+        codes, s = fp8.quantize_rows(hp.astype(np.float32), 128)
+        assert np.all((s_lo <= s) & (s <= s_hi))
+        v = fp8.e4m3_decode(codes)
+        assert np.all((v_lo <= v) & (v <= v_hi))
+    wide = np.count_nonzero(v_lo != v_hi)
+    assert 0 < wide < h.size // 4
+
+
+def test_h_bound_covers_a_float32_evaluation():
+    """The bound on a float32 evaluation of h = silu(x Wg) * (x Wu) holds for
+    an actual float32 evaluation (torch float32 matmuls on the CPU, silu in
+    float32), and is small against h."""
+    from oracle import moe
+    rng = np.random.default_rng(13)
+    n, K, I = 64, 2048, 256
+    x = rng.standard_normal((n, K))
+    wg = rng.standard_normal((K, I)) * 0.02
+    wu = rng.standard_normal((K, I)) * 0.02
+    g, u = x @ wg, x @ wu
+    h = moe.silu(g) * u
+    eps = moe.h_eval_bound(x, wg, wu, g, u)
+    t = lambda a: torch.from_numpy(a.astype(np.float32))
+    g32 = t(x) @ t(wg)
+    u32 = t(x) @ t(wu)
+    h32 = (torch.nn.functional.silu(g32) * u32).double().numpy()
+    assert np.all(np.abs(h32 - h) <= eps)
+    assert np.median(eps / np.abs(h)) < 1e-2
+
+
+def test_fp8_layer_allowance_covers_a_float32_evaluation():
+    """The FP8 layer evaluated in float32 (torch on the CPU: g and u, h,
+    h quantised by the oracle's own row quantiser, down) stays within the
+    oracle output plus its allowance, and every h code and scale of that
+    evaluation lies in the oracle's intervals."""
+    from oracle import moe
+    from synth import make_workload
+    wl = make_workload("fp8", seed=6, T=48, H=256, I=256, E=8, num_local=4,
+                       k=2)
+    ex = moe.expert_set_from_workload(wl)
+    res = moe.layer_from_workload(wl, ex, fp8_detail=True)
+    d = res.disp
+    x_rows = moe.activation_rows(wl.x, wl.act, "fp8")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    y = np.zeros((d.N, wl.H))
+    for p in range(wl.num_local):
+        rows = np.arange(d.offsets[p], d.offsets[p + 1])
+        if rows.size == 0:
+            continue
+        wg, wu, wd = ex.get(p)
+        xr = t(x_rows[d.row_token[rows]])
+        h32 = (torch.nn.functional.silu(xr @ t(wg)) * (xr @ t(wu))).numpy()
+        codes, s = fp8.quantize_rows(h32, 128)
+        assert np.all((res.fp8_routed.s_lo[rows] <= s) &
+                      (s <= res.fp8_routed.s_hi[rows]))
+        v = fp8.e4m3_decode(codes)
+        assert np.all((res.fp8_routed.v_lo[rows] <= v) &
+                      (v <= res.fp8_routed.v_hi[rows]))
+        y[rows] = fp8.dequantize_rows(codes, s, 128) @ wd
+    out = moe.combine(y, d.pair_row, res.weights, None, wl.T, wl.H)
+    rms = np.sqrt(np.mean(res.out ** 2))
+    assert np.all(np.abs(out - res.out) <= res.out_allow + 1e-9 * rms)

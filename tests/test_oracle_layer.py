@@ -153,3 +153,21 @@ def test_token_subset_matches_full_evaluation():
     sub = [0, 7, 29]
     part = moe.layer_from_workload(wl, ex, token_subset=sub)
     assert np.array_equal(part.out[sub], full.out[sub])
+
+
+def test_worker_threads_give_the_same_layer():
+    """Experts evaluated on worker threads: the same arithmetic, so the
+    same bits, for the plain and the FP8-detail paths."""
+    wl = make_workload("prefill", seed=9, T=40, H=64, I=32, E=16,
+                       num_local=8, k=4)
+    a = moe.layer_from_workload(wl)
+    b = moe.layer_from_workload(wl, workers=3)
+    assert np.array_equal(a.out, b.out)
+    f = make_workload("fp8", seed=9, T=24, H=256, I=128, E=8, num_local=4,
+                      k=2)
+    a = moe.layer_from_workload(f, fp8_detail=True)
+    b = moe.layer_from_workload(f, fp8_detail=True, workers=2)
+    assert np.array_equal(a.out, b.out)
+    assert np.array_equal(a.out_allow, b.out_allow)
+    assert np.array_equal(a.fp8_routed.v_lo, b.fp8_routed.v_lo,
+                          equal_nan=True)
