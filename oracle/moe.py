@@ -186,34 +186,48 @@ def swiglu(x64: np.ndarray, wg64: np.ndarray, wu64: np.ndarray,
     return h @ wd64
 
 
-# ---------------------------- what a float32 evaluation of h may differ by
+# ------------------------- what a correct evaluation of h may differ by (FP8)
 U32 = 2.0 ** -24           # unit roundoff of float32
-LAMBDA = 8.0               # scales of the accumulation error the bound allows
+LAMBDA = 4.0               # model standard deviations the bound allows
+# The FP8 recipe sums each 128-channel scale block's products as one unit
+# (the per-block scales apply to that sum).  gfx950's FP8 matrix instruction
+# returns such a 128-product sum with an error that is not float32 rounding
+# (only 11 % of the sums come back correctly rounded): mean-zero, with a root
+# mean square of 34 u * sum|p| over the block for normal-distributed codes
+# and 85 for the down projection's h codes times weight codes (measured
+# through the library; tests/test_gpu_fp8.py checks it stays within the
+# model).  The model takes 128, so LAMBDA = 4 model deviations is 15 of the
+# gate/up data's own.
+C_BLOCK = 128.0
 
 
 def h_eval_bound(x64: np.ndarray, wg64: np.ndarray, wu64: np.ndarray,
-                 g: np.ndarray, u: np.ndarray) -> np.ndarray:
-    """Bound on |h_fl32 - h| for h = silu(x Wg) * (x Wu) evaluated in float32.
-
-    Accumulation: g (and u) is a sum of K products p_k = x_k w_k.  Summed in
-    float32 in any fixed order (a matrix core's blocks included; the FP8
-    recipe's two per-block scale multiplies count as two more steps), the
-    error to first order is sum_i d_i S_i over the K + 2 operations, with
-    |d_i| <= u = 2^-24 independent and mean-zero for round-to-nearest, and
-    S_i the partial sums.  For the synthetic inputs the products are
-    independent zero-mean draws, so in any order that does not look at the
-    data the partial sums grow like a random walk, sum_i S_i^2 ~ (K^2 / 2)
-    mean(p^2) = (K / 2) ||p||^2, and the error is sub-Gaussian with scale
-    u sqrt(K / 2) ||p||.  The bound takes LAMBDA = 8 of those scales.
+                 g: np.ndarray, u: np.ndarray, block: int = 128) -> np.ndarray:
+    """Bound on |h_eval - h| for h = silu(x Wg) * (x Wu) evaluated by the FP8
+    recipe: each 128-product block sum S_b = sum_{k in b} x_k w_k comes back
+    with a mean-zero error of RMS at most C_BLOCK u sum_{k in b} |x_k w_k|,
+    independent between blocks, so the errors of g's blocks add like a random
+    walk: RMS C_BLOCK u sqrt(sum_b (sum_{k in b} |p_k|)^2); the bound takes
+    LAMBDA of those.  The scaled block sums are then multiplied by two scales
+    and added in float32 (round to nearest: at most (K/128 + 2) u sum|p|).
     silu(z) = z / (1 + exp(-z)): |silu'| <= 1.1, and its float32 evaluation
     (the exponent's argument rounded, exp to within 2 ulp, one add, one
     divide) has relative error below (|z| + 6) u; the bound takes twice that.
     The product silu(g) * u adds one rounding."""
     K = x64.shape[1]
-    scale = LAMBDA * U32 * np.sqrt((K + 2.0) / 2.0)
-    x2 = x64 * x64
-    eg = scale * np.sqrt(x2 @ (wg64 * wg64))
-    eu = scale * np.sqrt(x2 @ (wu64 * wu64))
+    nb = K // block
+    ax = np.abs(x64)
+
+    def bound(w64):
+        aw = np.abs(w64)
+        sq = np.zeros((x64.shape[0], w64.shape[1]))
+        for b in range(nb):
+            sb = ax[:, b * block:(b + 1) * block] @ aw[b * block:(b + 1) * block]
+            sq += sb * sb
+        return (LAMBDA * C_BLOCK * U32 * np.sqrt(sq) +
+                (nb + 2) * U32 * (ax @ aw))
+
+    eg, eu = bound(wg64), bound(wu64)
     sg = silu(g)
     es = 1.1 * eg + 2.0 * (np.abs(g) + 6.0) * U32 * np.abs(sg)
     h = sg * u
@@ -223,9 +237,9 @@ def h_eval_bound(x64: np.ndarray, wg64: np.ndarray, wu64: np.ndarray,
 @dataclasses.dataclass
 class Fp8Rows:
     """Per routed (or shared) row of the FP8 recipe: the exact h, the
-    interval of scales and E4M3 code values a correct float32 evaluation may
-    produce for it (a value near a rounding boundary has two correct codes),
-    and the largest change of the dequantised h that choice allows."""
+    interval of scales and E4M3 code values a correct evaluation may produce
+    for it (a value near a rounding boundary has two correct codes), and the
+    largest change of the dequantised h that choice allows."""
     h: np.ndarray            # [n, I] float64, exact silu(x Wg) * (x Wu)
     s_lo: np.ndarray         # [n, I/128] float32
     s_hi: np.ndarray
@@ -240,7 +254,7 @@ def fp8_rows_detail(x64, wg64, wu64, block: int = 128):
     g = x64 @ wg64
     u = x64 @ wu64
     h = silu(g) * u
-    eps = h_eval_bound(x64, wg64, wu64, g, u)
+    eps = h_eval_bound(x64, wg64, wu64, g, u, block)
     s_lo, s_hi = _fp8.row_scale_interval(h, eps, block)
     v_lo, v_hi = _fp8.row_code_interval(h, eps, s_lo, s_hi, block)
     slo = np.repeat(s_lo.astype(np.float64), block, axis=1)

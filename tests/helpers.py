@@ -122,6 +122,7 @@ def run_fp8_steps(wl, layout="kn"):
         np.float32).reshape(rows, I // 128)
     got = dict(offsets=off, row_token=b.row_token.cpu().numpy()[:N],
                h=h.copy(), h_scales=hs.copy(), cap=cap,
+               y_perm=b.y_perm.cpu().numpy()[: N * wl.H].reshape(N, wl.H),
                out=out_to_f64(b, wl))
     # the layer forward on the same inputs and weights
     b2 = dl.buffers()
@@ -219,3 +220,16 @@ def _take_rows(det, rows):
     return _m.Fp8Rows(h=det.h[rows], s_lo=det.s_lo[rows], s_hi=det.s_hi[rows],
                       v_lo=det.v_lo[rows], v_hi=det.v_hi[rows],
                       allow=det.allow[rows])
+
+
+def fp8_complete_check(wl, tokens=None, layout="kn", workers=0):
+    """Run the FP8 layer step by step and as one forward (they must agree
+    bit for bit) and apply check_fp8_complete against the oracle."""
+    print(f"layer {wl.describe()} layout={layout}", flush=True)
+    got = run_fp8_steps(wl, layout=layout)
+    assert np.array_equal(got["out"], got["out_layer"])
+    ref = omoe.layer_from_workload(wl, token_subset=tokens, fp8_detail=True,
+                                   workers=workers)
+    st = check_fp8_complete(wl, got, ref, tokens)
+    print(f"  {st}", flush=True)
+    return st

@@ -10,8 +10,8 @@ import pytest
 from oracle import eplb, moe as omoe
 from synth import make_workload
 
-from .helpers import (BARS, check_output, device_layer, out_to_f64,
-                      phys_to_logical_from_map, recipe)
+from .helpers import (BARS, check_output, device_layer, fp8_complete_check,
+                      out_to_f64, phys_to_logical_from_map, recipe)
 
 pytestmark = pytest.mark.gpu
 
@@ -194,8 +194,11 @@ def test_layer_hot_expert(name, kw):
     wl = with_hot_expert(make_workload(name, seed=17, **kw), 3)
     print(f"layer hot expert 3: {wl.describe()}", flush=True)
     out, counts = run_layer(wl)
-    ref = oracle_out(wl)
     assert counts[3] == wl.T
+    if wl.wdt == "fp8":           # several h codes can be correct
+        fp8_complete_check(wl)
+        return
+    ref = oracle_out(wl)
     assert np.array_equal(counts, ref.counts)
     check_output(out, ref.out, wl.out, BARS[recipe(wl)], wl.describe())
 
@@ -208,6 +211,9 @@ def test_layer_hot_expert(name, kw):
 def test_layer_single_token(name, kw):
     wl = make_workload(name, seed=19, **kw)
     print(f"layer {wl.describe()}", flush=True)
+    if wl.wdt == "fp8":
+        fp8_complete_check(wl)
+        return
     out, _ = run_layer(wl)
     ref = oracle_out(wl)
     check_output(out, ref.out, wl.out, BARS[recipe(wl)], wl.describe())

@@ -169,9 +169,9 @@ def test_perturbed_quantisations_stay_inside_the_intervals():
 
 
 def test_h_bound_covers_a_float32_evaluation():
-    """The bound on a float32 evaluation of h = silu(x Wg) * (x Wu) holds for
-    an actual float32 evaluation (torch float32 matmuls on the CPU, silu in
-    float32), and is small against h."""
+    """The bound on an evaluation of h = silu(x Wg) * (x Wu) covers an actual
+    float32 evaluation (torch float32 matmuls on the CPU, silu in float32),
+    and is small against h."""
     from oracle import moe
     rng = np.random.default_rng(13)
     n, K, I = 64, 2048, 256
@@ -221,3 +221,32 @@ def test_fp8_layer_allowance_covers_a_float32_evaluation():
     out = moe.combine(y, d.pair_row, res.weights, None, wl.T, wl.H)
     rms = np.sqrt(np.mean(res.out ** 2))
     assert np.all(np.abs(out - res.out) <= res.out_allow + 1e-9 * rms)
+
+
+def test_h_bound_covers_block_sums_with_the_modelled_error():
+    """Brute force of the model behind the bound: every 128-product block
+    sum of g and u perturbed by a normal error of RMS C_BLOCK u sum|p| over
+    the block (independent between blocks), h recomputed in float64: the
+    result stays within the bound."""
+    from oracle import moe
+    rng = np.random.default_rng(14)
+    n, K, I, B = 24, 1024, 128, 128
+    x = rng.standard_normal((n, K))
+    wg = rng.standard_normal((K, I)) * 0.02
+    wu = rng.standard_normal((K, I)) * 0.02
+    g, u = x @ wg, x @ wu
+    h = moe.silu(g) * u
+    eps = moe.h_eval_bound(x, wg, wu, g, u, B)
+
+    def perturbed(w):
+        tot = np.zeros((n, I))
+        for b in range(K // B):
+            xb, wb = x[:, b * B:(b + 1) * B], w[b * B:(b + 1) * B]
+            sb = xb @ wb
+            rms = moe.C_BLOCK * moe.U32 * (np.abs(xb) @ np.abs(wb))
+            tot += sb + rms * rng.standard_normal(sb.shape)
+        return tot
+
+    for _ in range(5):
+        hp = moe.silu(perturbed(wg)) * perturbed(wu)
+        assert np.all(np.abs(hp - h) <= eps)
