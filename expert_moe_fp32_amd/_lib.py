@@ -69,6 +69,14 @@ def lib() -> ctypes.CDLL:
             raise ImportError(
                 f"{LIB_PATH} is missing: build it with "
                 "`python -m expert_moe_fp32_amd.build` (hipcc, gfx950)")
+        # torch brings its own HIP runtime (same soname as the system one the
+        # library links against); loading it first makes the library bind to
+        # that one copy, so the process holds a single HIP runtime whatever
+        # the order of first use
+        try:
+            import torch  # noqa: F401
+        except ImportError:  # pragma: no cover - the binding needs torch
+            pass
         L = ctypes.CDLL(LIB_PATH)
         P, V, S, I32 = (ctypes.POINTER(Problem), ctypes.c_void_p,
                         ctypes.c_size_t, ctypes.c_int32)
