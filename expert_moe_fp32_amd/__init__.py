@@ -11,6 +11,7 @@ from ._lib import (MOE_LAYOUT_KN, MOE_LAYOUT_NK,  # noqa: F401
                    moe_eplb_hottest_map, moe_eplb_plan, moe_eplb_rank_map,
                    moe_eplb_record_load, moe_ffn_intermediate,
                    moe_ffn_workspace_size, moe_grouped_ffn,
-                   moe_layer_forward, moe_layer_workspace_size,
+                   moe_layer_forward, moe_layer_forward_noalloc,
+                   moe_layer_workspace_size,
                    moe_prepack_weights, moe_quantize_fp8_blocks,
                    moe_route_topk, moe_workspace_size, status_string)

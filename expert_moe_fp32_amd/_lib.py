@@ -29,7 +29,8 @@ EXPORTS = (
     "moe_dispatch_workspace_size",
     "moe_ffn_workspace_size", "moe_layer_workspace_size", "moe_route_topk",
     "moe_dispatch", "moe_grouped_ffn", "moe_ffn_intermediate", "moe_combine",
-    "moe_layer_forward", "moe_layer_forward_timed", "moe_prepack_weights",
+    "moe_layer_forward", "moe_layer_forward_timed",
+    "moe_layer_forward_noalloc", "moe_prepack_weights",
     "moe_quantize_fp8_blocks",
     "moe_eplb_hottest_map", "moe_eplb_plan", "moe_eplb_rank_map",
     "moe_eplb_record_load",
@@ -103,6 +104,8 @@ def lib() -> ctypes.CDLL:
                                                        ctypes.POINTER(Weights),
                                                        V, V, V, V, V, S, V,
                                                        V]),
+            "moe_layer_forward_noalloc": (ctypes.c_int, [
+                P, V, V, V, ctypes.POINTER(Weights), V, V, V, V, V]),
             "moe_prepack_weights": (ctypes.c_int, [V, I32, I32, I32, I32, V,
                                                    V]),
             "moe_quantize_fp8_blocks": (ctypes.c_int, [V, I32, I32, I32, I32,
@@ -269,6 +272,24 @@ def moe_layer_forward_timed(p, logits, bias, x, weights: Weights, l2p,
         ctypes.addressof(ev))
     if check:
         _check(st, "moe_layer_forward_timed")
+    return st
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_layer_forward_noalloc(p, logits, bias, x, weights: Weights, l2p,
+                              replica_count, out, expert_counts, stream=None,
+                              check=True) -> int:
+    """moe_layer_forward with the library's own device scratch (no
+    workspace argument; for callers that cannot allocate)."""
+    st = lib().moe_layer_forward_noalloc(
+        ctypes.byref(p), ptr(logits), ptr(bias), ptr(x),
+        ctypes.byref(weights), ptr(l2p), ptr(replica_count), ptr(out),
+        ptr(expert_counts),
+        stream if stream is not None else current_stream())
+    if check:
+        _check(st, "moe_layer_forward_noalloc")
     return st
 
 

@@ -39,7 +39,8 @@
  *    and a map entry outside [0, P) drops its pair (pair_row -1).
  *  - T = 0 is valid: the call enqueues nothing and succeeds (an idle rank's
  *    dummy forward, infra-guide page, section 4.3).
- *  - Re-entrant; no global mutable state.
+ *  - Re-entrant; no global mutable state, except the per-device scratch of
+ *    moe_layer_forward_noalloc (see there).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -276,6 +277,31 @@ MOE_API moe_status moe_layer_forward_timed(const moe_problem* p,
                                    int32_t* expert_counts, void* workspace,
                                    size_t ws_bytes, void* stream,
                                    void* const* events);
+
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same work, with the workspace taken from a device array
+ * the library holds, MOE_NOALLOC_SCRATCH_BYTES on each GPU it runs on (kept
+ * until the process ends), instead of a caller's buffer.  The call itself
+ * allocates nothing.  WORKSPACE when the problem needs more than that
+ * (moe_layer_workspace_size; e.g. a 256-token decode batch at H = 6144,
+ * I = 2048, 32 local experts needs 56 MiB).  Every call on one GPU shares
+ * its array and the array keeps the last call's contents (the layer needs
+ * none of them: whatever must start at zero is cleared by its kernels), so
+ * calls that overlap on one GPU -- on different streams, or from different
+ * threads -- race; calls one after another on one stream do not.  The
+ * array's address on each device is looked up once, on that device's first
+ * call (the device of `stream`, or the current device for the null
+ * stream). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+MOE_API moe_status moe_layer_forward_noalloc(const moe_problem* p,
+                                             const float* logits,
+                                             const float* bias, const void* x,
+                                             const moe_weights* w,
+                                             const int32_t* l2p,
+                                             const int32_t* replica_count,
+                                             void* out, int32_t* expert_counts,
+                                             void* stream);
 
 /* One-time weight preparation (not on the layer's path): a matrix with
  * reduction size K and N output channels, stored as `layout` says (see
