@@ -17,6 +17,9 @@ always-on shared expert, one EP rank's contiguous share of experts):
   skew as the power-law load simulation of the infra-guide page, section 5.2).
 * ``fp8``     DeepSeek-V3 shape, T=4096, no shared expert; fp32 master weights
   that each side quantises to OCP E4M3 with one fp32 scale per 128x128 block.
+* ``decode_skewed`` ``decode`` plus the Zipf s=1.2 logit bias of ``skewed``:
+  a decode batch in which one local expert holds several times the mean
+  rows (51-166 of 138-275 local rows over four seeds).
 * ``lowlat``  the low-latency decode setting of DeepEP's low-latency kernels as
   the infra-guide page, section 6.1, gives it: 128 tokens a batch, hidden 7168,
   top-8, FP8 dispatch (activations in E4M3 per token per 128 channels) and
@@ -63,6 +66,10 @@ CONFIGS: Dict[str, dict] = {
     "lowlat": dict(wid=6, T=128, H=7168, I=2048, E=256, k=8, expert_begin=0,
                    num_local=32, shared=False, act="bf16", wdt="fp8",
                    out="bf16", bias=None, quant_block=128),
+    "decode_skewed": dict(wid=7, T=256, H=6144, I=2048, E=256, k=8,
+                          expert_begin=0, num_local=32, shared=False,
+                          act="bf16", wdt="bf16", out="bf16", bias="zipf",
+                          zipf_s=1.2),
 }
 
 _TENSOR_LOGITS, _TENSOR_X, _TENSOR_W, _TENSOR_SHARED, _TENSOR_PERM = 1, 2, 3, 4, 5
