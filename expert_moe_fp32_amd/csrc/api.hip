@@ -58,6 +58,15 @@ DispatchScratch carve_dispatch(Carver& c, const moe_problem* p) {
   return d;
 }
 
+// Expected rows per physical expert: the local pairs over the physical
+// experts, where a rank with fewer physical than logical experts (a
+// group-wide placement whose other replicas sit on other ranks) expects
+// about one logical expert's pairs per physical expert.
+int rows_hint(const moe_problem* p) {
+  const double pairs = (double)p->T * p->k * p->num_local / p->E;
+  return (int)(pairs / std::max(p->num_physical, p->num_local) + 0.5);
+}
+
 struct FfnScratch {
   void* h;
   float* h_scales;
@@ -77,7 +86,11 @@ FfnScratch carve_ffn(Carver& c, const moe_problem* p) {
   f.h = c.take<char>(hrows * p->I * hb);
   if (p->weight_dtype == MOE_FP8_E4M3) {
     f.h_scales = c.take<float>(hrows * (p->I / 128));
-    f.h32 = c.take<float>(hrows * p->I);
+    // float32 h only for the kernels that leave quantisation to a pass of
+    // its own (the 32-row register-streaming kernel quantises in place)
+    int balanced;
+    if (ffn_fp8_tile_rows(rows_hint(p), p->H, p->I, &balanced) != 32)
+      f.h32 = c.take<float>(hrows * p->I);
   }
   f.max_tiles = (int)(p->num_physical + 1 + (hrows + 15) / 16 + 1);
   f.tiles = c.take<int4>((size_t)f.max_tiles);
@@ -85,15 +98,6 @@ FfnScratch carve_ffn(Carver& c, const moe_problem* p) {
   f.tiles_down = c.take<int4>((size_t)p->num_physical + 2 + hrows / 128);
   f.tile_count = c.take<int32_t>(4);
   return f;
-}
-
-// Expected rows per physical expert: the local pairs over the physical
-// experts, where a rank with fewer physical than logical experts (a
-// group-wide placement whose other replicas sit on other ranks) expects
-// about one logical expert's pairs per physical expert.
-int rows_hint(const moe_problem* p) {
-  const double pairs = (double)p->T * p->k * p->num_local / p->E;
-  return (int)(pairs / std::max(p->num_physical, p->num_local) + 0.5);
 }
 
 moe_status launch_ffn_common(const moe_problem* p, const void* x_perm,

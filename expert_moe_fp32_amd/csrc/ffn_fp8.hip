@@ -44,7 +44,9 @@ struct K8Args {
   const void* w1_sh;
   const float* s0_sh;
   const float* s1_sh;
-  float* h_out;               // gate/up: float32 h [cap + T][N]
+  float* h_out;               // gate/up (128 x 128 tiles): float32 h [cap + T][N]
+  uint8_t* hq_out;            // gate/up (streaming kernels): E4M3 codes of h
+  float* hs_out;              //   [cap + T][N], scales [cap + T][N/128]
   float* y_routed;            // down: [cap][N]
   float* y_shared;            // down: [T][N]
 };
@@ -240,6 +242,61 @@ __global__ __launch_bounds__(256) void k_tile_fp8(K8Args a) {
 }
 
 // ------------------------------------------------------ LDS-ring kernel
+// Maximum over the 16 lanes of a DPP row (every lane gets it).
+__device__ __forceinline__ float row16_max(float v) {
+#define ROWF(ctrl)                                                            \
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(                    \
+                   0, __float_as_int(v), ctrl, 0xF, 0xF, false)));
+  ROWF(0x128) ROWF(0x124) ROWF(0x122) ROWF(0x121)
+#undef ROWF
+  return v;
+}
+
+// Gate/up epilogue of the streaming kernels, whose item covers one 128-
+// channel group of h (= one quantisation group): h = silu(g) * u per element,
+// then E4M3 per row over the group (scale = amax/448, 1 for an all-zero
+// group; code = RNE of fl32(h / scale), saturated), the same float32 steps
+// as k_quant_h_fp8.  A wavefront holds CW channels of each of its rows; the
+// group's amax is the maximum of the partial maxima the item's wavefronts
+// leave in LDS (pmax [NCW][rows]), and the codes are assembled in an LDS
+// byte tile [rows][128] and stored 16 bytes a lane.  Called by the whole
+// workgroup once every wavefront's transfers have landed; pmax and tile lie
+// in ring slots no transfer writes any more.
+struct HQuant {
+  float* pmax;                // LDS [NCW * ROWS], then scale [ROWS]
+  uint8_t* tile;              // LDS [ROWS * 128]
+  int rows_cap;               // ROWS (rows of the tile, padded)
+  float* scale;               // LDS [ROWS]: pmax + NCW * ROWS
+};
+
+// One thread per row: the group's amax from the NCW partial maxima, its
+// scale into LDS and, for real rows, into the h scale rows.
+__device__ __forceinline__ void hq_scales(const HQuant& q, const K8Args& a,
+                                          bool sh, int row0, int nrows,
+                                          int nb, int ncw, int nthreads) {
+  float* out = a.hs_out + ((size_t)(sh ? a.cap : 0) + row0) * (a.N / 128) + nb;
+  for (int lr = threadIdx.x; lr < q.rows_cap; lr += nthreads) {
+    float amax = q.pmax[lr];
+    for (int w = 1; w < ncw; ++w) amax = fmaxf(amax, q.pmax[w * q.rows_cap + lr]);
+    const float sc = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+    q.scale[lr] = sc;
+    if (lr < nrows) out[(size_t)lr * (a.N / 128)] = sc;
+  }
+}
+
+__device__ __forceinline__ void hq_store(const HQuant& q, const K8Args& a,
+                                         bool sh, int row0, int nrows, int nb,
+                                         int nthreads) {
+  // codes of rows < nrows to the h code rows, 128 bytes a row
+  const int N = a.N;
+  uint8_t* dst = a.hq_out + ((size_t)(sh ? a.cap : 0) + row0) * N + nb * 128;
+  for (int i = threadIdx.x; i < nrows * 8; i += nthreads) {
+    const int r = i >> 3, c = i & 7;
+    *(u32x4_t*)(dst + (size_t)r * N + 16 * c) =
+        *(const u32x4_t*)(q.tile + r * 128 + 16 * c);
+  }
+}
+
 // For groups of up to 16 * NMB = 160 rows (one tile per expert at
 // prefill-like batches of ~130 rows per expert).  A workgroup of 8
 // wavefronts owns one tile and a group of output channels; each wavefront
@@ -701,14 +758,45 @@ __global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
 #undef RING_STEP
     }
     WAIT_VMCNT(0);                               // trailing re-reads landed
+    if (MODE == M8_GATEUP) {
+      // h quantised here: wavefront wv holds channels 16 wv .. 16 wv + 15 of
+      // the group for every row; partial maxima in la0, codes in la1
+      HQuant hq{(float*)la0, (uint8_t*)la1, 16 * NMB, (float*)la0 + 8 * 16 * NMB};
+      // h overwrites the gate accumulators (no registers beyond them)
+#pragma unroll
+      for (int m = 0; m < NMB; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[m][0][r] = silu_f32(acc[m][0][r]) * acc[m][1][r];
+      auto hv = [&](int m, int r) -> float { return acc[m][0][r]; };
+      lds_barrier();                             // every wavefront past the ring
+#pragma unroll
+      for (int m = 0; m < NMB; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = row16_max(fabsf(hv(m, r)));
+          if (c16 == 0) hq.pmax[wv * hq.rows_cap + m * 16 + 4 * q + r] = v;
+        }
+      lds_barrier();
+      hq_scales(hq, a, sh, row0, nrows, nb, 8, 512);
+      lds_barrier();
+#pragma unroll
+      for (int m = 0; m < NMB; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lr = m * 16 + 4 * q + r;
+          hq.tile[lr * 128 + wv * 16 + c16] =
+              f32_to_e4m3(__fdiv_rn(hv(m, r), hq.scale[lr]));
+        }
+      lds_barrier();
+      hq_store(hq, a, sh, row0, nrows, nb, 512);
+      continue;
+    }
     // Epilogue from a wave-uniform 64-bit base and 32-bit offsets; N goes
     // through an opaque move so the offsets are formed here rather than
     // hoisted out of the item loop (hoisted, they spilled).
     int N;
     asm volatile("s_mov_b32 %0, %1" : "=s"(N) : "s"(a.N));
-    float* out = MODE == M8_GATEUP
-                     ? a.h_out + ((size_t)(sh ? a.cap : 0) + row0) * N + cb0 * 16
-                     : (sh ? a.y_shared : a.y_routed) + (size_t)row0 * N + cb0 * 16;
+    float* out = (sh ? a.y_shared : a.y_routed) + (size_t)row0 * N + cb0 * 16;
 #pragma unroll
     for (int m = 0; m < NMB; ++m) {
       if (m >= nmb) continue;
@@ -717,12 +805,8 @@ __global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
         const int lr = m * 16 + 4 * q + r;
         if (lr >= nrows) continue;
         const int off = lr * N + c16;
-        if (MODE == M8_GATEUP) {
-          out[off] = silu_f32(acc[m][0][r]) * acc[m][1][r];
-        } else {
-          out[off] = acc[m][0][r];
-          out[off + (cb1 - cb0) * 16] = acc[m][1][r];
-        }
+        out[off] = acc[m][0][r];
+        out[off + (cb1 - cb0) * 16] = acc[m][1][r];
       }
     }
   }
@@ -731,14 +815,6 @@ __global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
 // Quantise float32 h rows per 128 channels: routed rows [0, N) (N read on the
 // device) and shared rows [cap, cap + T_sh).  A lane takes 8 channels (two
 // 16-byte loads), the 16 lanes of a DPP row one 128-channel group.
-__device__ __forceinline__ float row16_max(float v) {
-#define ROWF(ctrl)                                                            \
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(                    \
-                   0, __float_as_int(v), ctrl, 0xF, 0xF, false)));
-  ROWF(0x128) ROWF(0x124) ROWF(0x122) ROWF(0x121)
-#undef ROWF
-  return v;
-}
 
 __global__ __launch_bounds__(256) void k_quant_h_fp8(
     const float* __restrict__ h, int I, const int32_t* __restrict__ n_routed,
@@ -829,6 +905,8 @@ hipError_t launch_ffn_fp8(FfnArgs& f, hipStream_t s) {
   a.s0_sh = w->sh_s_gate;
   a.s1_sh = w->sh_s_up;
   a.h_out = f.h32;
+  a.hq_out = (uint8_t*)f.h;
+  a.hs_out = f.h_scales;
   a.nb_per_tile = a.N / (stream ? 128 : 64);
   long items = max_tiles * a.nb_per_tile;
   long grid = items < cu * 2 ? items : cu * 2;
@@ -839,8 +917,12 @@ hipError_t launch_ffn_fp8(FfnArgs& f, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (f.events) hipEventRecord(f.events[1], s);   // gate/up kernel alone
-  // ---- h -> E4M3 per row per 128 channels
-  {
+  // ---- h -> E4M3 per row per 128 channels.  The register-streaming kernel
+  // (32-row tiles) quantises in its epilogue.  The LDS ring (160-row tiles)
+  // and the 128 x 128 tiles write float32 h for this pass: a fused epilogue
+  // in the ring held its workgroup off the weight stream for four barriers
+  // per item (FP8 layer 489 -> 502 us).
+  if (BM != 32) {
     long qg = (hrows * (f.I / 8) + 255) / 256;
     if (qg > 8192) qg = 8192;
     if (qg < 1) qg = 1;

@@ -25,6 +25,8 @@
 // share their A rows; a round of the persistent loop gives each XCD a
 // contiguous run of items, so the workgroups of one XCD share one tile's A
 // rows through that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -67,19 +69,25 @@ __device__ __forceinline__ f32x16_t mfma32b(u32x4_t a, u32x4_t b, f32x16_t c) {
 // queue stalled the issuing wavefront for hundreds of cycles when all
 // transfers of a stage went out at once after the barrier) and the LDS
 // work while the MFMAs run.
-template <int NV>
+// NM MFMAs, NV DMA transfers and NR fragment reads in the step.
+template <int NV, int NM, int NR>
 __device__ __forceinline__ void interleave() {
+  constexpr int MD = NV < NM ? NV : NM;          // MFMAs paired with a DMA
+  constexpr int PR = (NR + 1) / 2;               // read pairs
+  constexpr int MR = PR < NM - MD ? PR : NM - MD;  // MFMAs paired with reads
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
+  for (int i = 0; i < MD; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
+  if (NV > MD) __builtin_amdgcn_sched_group_barrier(0x020, NV - MD, 0);
 #pragma unroll
-  for (int i = 0; i < 6; ++i) {
+  for (int i = 0; i < MR; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 16 - NV - 6, 0);
+  if (NR > 2 * MR) __builtin_amdgcn_sched_group_barrier(0x100, NR - 2 * MR, 0);
+  if (NM > MD + MR) __builtin_amdgcn_sched_group_barrier(0x008, NM - MD - MR, 0);
 }
 
 // Workgroup = WM x WN wavefronts; wavefront (wm, wn) owns TM x TN blocks of
@@ -178,8 +186,12 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
     // of a read take 16 distinct 16-byte bank groups (row parity x slot).
     // A wavefront whose rows are all padding multiplies them too (its
     // stores are skipped), which keeps the step one basic block.
-    auto load = [&](const u32x4_t* A, int HH, const u32x4_t* B,
+    // Only the wavefront's first NMB row blocks hold tile rows (the rest
+    // are padding of a partial tile): their fragments are read and
+    // multiplied, the others skipped.
+    auto load = [&](auto nmb_c, const u32x4_t* A, int HH, const u32x4_t* B,
                     u32x4_t (&fa)[2][TM], u32x4_t (&fb)[2][TN]) {
+      constexpr int NMB = decltype(nmb_c)::value;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int pos = c16 + 16 * (2 * s + ks);   // lane slot inside a B block
@@ -193,14 +205,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
           fb[s][j] = B[(2 * cb32 + hi) * 64 + pos];
         }
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[s][i] = A[(wm * TM + i) * 4 * 64 + apos];
+        for (int i = 0; i < NMB; ++i) fa[s][i] = A[(wm * TM + i) * 4 * 64 + apos];
       }
     };
-    auto mma = [&](const u32x4_t (&fa)[2][TM], const u32x4_t (&fb)[2][TN]) {
+    auto mma = [&](auto nmb_c, const u32x4_t (&fa)[2][TM],
+                   const u32x4_t (&fb)[2][TN]) {
+      constexpr int NMB = decltype(nmb_c)::value;
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < NMB; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j) acc[i][j] = mfma32b(fa[s][i], fb[s][j], acc[i][j]);
     };
@@ -226,29 +240,52 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(GArgs a) {
     issue_b(3, lb3);
     WAIT_VMCNT(3 * HB + HA);             // stage 0
     lds_barrier();
-    load(pa0, 0, lb0, fa0, fb0);
     const int last_pair = KT / 2 - 1;
-    for (int kt = 0; kt < KT; kt += 4) {
-#define GEMM_STEP(S, PA1, HH1, BC1, PN, BN_, FC_A, FC_B, FN_A, FN_B)          \
-      {                                                                      \
-        const int k = kt + S;                                                \
-        if (S % 2 == 0) WAIT_VMCNT(2 * HB + HA);                             \
-        else WAIT_VMCNT(HB);                                                 \
-        lds_barrier();                                                       \
-        __builtin_amdgcn_sched_barrier(0);                                   \
-        issue_b(k + 4 < KT ? k + 4 : KT - 1, BN_);                           \
-        if (S % 2 == 1) issue_a((k + 3) / 2 < last_pair ? (k + 3) / 2 : last_pair, PN); \
-        load(PA1, HH1, BC1, FN_A, FN_B);                                     \
-        mma(FC_A, FC_B);                                                     \
-        interleave<S % 2 == 1 ? HB + HA : HB>();                             \
-        __builtin_amdgcn_sched_barrier(0);                                   \
-      }
-      GEMM_STEP(0, pa0, 1, lb1, pa0, lb0, fa0, fb0, fa1, fb1)
-      GEMM_STEP(1, pa1, 0, lb2, pa0, lb1, fa1, fb1, fa0, fb0)
-      GEMM_STEP(2, pa1, 1, lb3, pa1, lb2, fa0, fb0, fa1, fb1)
-      GEMM_STEP(3, pa0, 0, lb0, pa1, lb3, fa1, fb1, fa0, fb0)
-#undef GEMM_STEP
+    // The K loop for a wavefront with NMB row blocks of tile rows (a
+    // wave-uniform choice per item; a wavefront without any still issues
+    // its share of the transfers and meets every barrier).  Written out
+    // once per NMB by a macro rather than as a lambda: through a lambda the
+    // fragment reads lost track of which LDS slots the transfers write, and
+    // the compiler waited for all transfers before every read.
+#define GEMM_STEP(NMB, S, PA1, HH1, BC1, PN, BN_, FC_A, FC_B, FN_A, FN_B)     \
+    {                                                                        \
+      const int k = kt + S;                                                  \
+      if (S % 2 == 0) WAIT_VMCNT(2 * HB + HA);                               \
+      else WAIT_VMCNT(HB);                                                   \
+      lds_barrier();                                                         \
+      __builtin_amdgcn_sched_barrier(0);                                     \
+      issue_b(k + 4 < KT ? k + 4 : KT - 1, BN_);                             \
+      if (S % 2 == 1) issue_a((k + 3) / 2 < last_pair ? (k + 3) / 2 : last_pair, PN); \
+      if ((NMB) > 0) {                                                       \
+        load(std::integral_constant<int, (NMB)>{}, PA1, HH1, BC1, FN_A, FN_B); \
+        mma(std::integral_constant<int, (NMB)>{}, FC_A, FC_B);                 \
+      }                                                                      \
+      interleave<(S % 2 == 1 ? HB + HA : HB), (2 * (NMB) * TN),               \
+                 ((NMB) > 0 ? 2 * ((NMB) + TN) : 0)>();                      \
+      __builtin_amdgcn_sched_barrier(0);                                     \
     }
+#define GEMM_K_LOOP(NMB)                                                     \
+    {                                                                        \
+      if ((NMB) > 0) load(std::integral_constant<int, (NMB)>{}, pa0, 0, lb0, fa0, fb0); \
+      for (int kt = 0; kt < KT; kt += 4) {                                   \
+        GEMM_STEP(NMB, 0, pa0, 1, lb1, pa0, lb0, fa0, fb0, fa1, fb1)         \
+        GEMM_STEP(NMB, 1, pa1, 0, lb2, pa0, lb1, fa1, fb1, fa0, fb0)         \
+        GEMM_STEP(NMB, 2, pa1, 1, lb3, pa1, lb2, fa0, fb0, fa1, fb1)         \
+        GEMM_STEP(NMB, 3, pa0, 0, lb0, pa1, lb3, fa1, fb1, fa0, fb0)         \
+      }                                                                      \
+    }
+    {
+      int nmb = (nrows - wm * TM * 32 + 31) / 32;   // wave-uniform
+      nmb = nmb < 0 ? 0 : (nmb > TM ? TM : nmb);
+      nmb = __builtin_amdgcn_readfirstlane(nmb);
+      if (nmb == TM) GEMM_K_LOOP(TM)
+      else if (nmb == 0) GEMM_K_LOOP(0)
+      else if (nmb == 1) GEMM_K_LOOP(1)
+      else if (nmb == 2) GEMM_K_LOOP((TM > 2 ? 2 : 1))
+      else GEMM_K_LOOP((TM > 3 ? 3 : 1))
+    }
+#undef GEMM_K_LOOP
+#undef GEMM_STEP
     WAIT_VMCNT(0);                       // the trailing re-reads have landed
     // Epilogue, one row block at a time: a wave-uniform 64-bit base per
     // block and 32-bit lane offsets.  N and the lane's row half are read
