@@ -92,7 +92,10 @@ FfnScratch carve_ffn(Carver& c, const moe_problem* p) {
     if (ffn_fp8_tile_rows(rows_hint(p), p->H, p->I, &balanced) != 32)
       f.h32 = c.take<float>(hrows * p->I);
   }
-  f.max_tiles = (int)(p->num_physical + 1 + (hrows + 15) / 16 + 1);
+  // descriptors: at most one per 16 rows plus one per group, and the four
+  // quarters of a tall tile (groups of more than 32 rows) at most one per 8
+  // rows of their group
+  f.max_tiles = (int)(p->num_physical + 2 + (hrows + 15) / 16 + (hrows + 7) / 8);
   f.tiles = c.take<int4>((size_t)f.max_tiles);
   // 128-row tiles: at most one partial tile per group
   f.tiles_down = c.take<int4>((size_t)p->num_physical + 2 + hrows / 128);
@@ -478,6 +481,7 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
   extras.tile_count = L.f.tile_count;
   extras.BM = ffn_tile_rows(p->act_dtype, p->weight_dtype, rows_hint(p),
                             p->H, p->I, &extras.balanced);
+  extras.tallBM = ffn_tall_rows(p->act_dtype, p->weight_dtype, extras.BM);
   extras.has_shared = p->has_shared;
   if (launch_route_topk(logits, bias, p->T, p->E, p->k, L.ids, L.tw,
                         nullptr, s) != hipSuccess)

@@ -68,6 +68,37 @@ __device__ __forceinline__ int tile_split(int rows, int BM, int balanced,
   return (rows + p - 1) / p;
 }
 
+// Tiles of one group under a per-group choice: a group of more than BM rows
+// is cut into (balanced) tall tiles of up to tallBM rows, each listed four
+// times as quarters (the streaming kernel then reads each weight byte once
+// per tall tile instead of once per BM rows); otherwise tile_split(rows, BM,
+// balanced).  tallBM = 0 keeps one tile height for every group.  Returns
+// the number of descriptors; *tall says whether they are quarters (the
+// fourth descriptor field then holds 1 + quarter).
+__device__ __forceinline__ int group_tiles(int rows, int BM, int balanced,
+                                           int tallBM, int* per, int* tall) {
+  if (tallBM > 0 && rows > BM) {
+    *tall = 1;
+    return 4 * tile_split(rows, tallBM, 1, per);
+  }
+  *tall = 0;
+  return tile_split(rows, BM, balanced, per);
+}
+
+// Writes the descriptors of one group from index i on (see group_tiles).
+__device__ __forceinline__ void write_group_tiles(int4* tiles, int i, int g,
+                                                  int start, int rows, int per,
+                                                  int tall) {
+  for (int r = 0; r < rows; r += per) {
+    const int n = min(per, rows - r);
+    if (tall) {
+      for (int qd = 0; qd < 4; ++qd) tiles[i++] = make_int4(g, start + r, n, 1 + qd);
+    } else {
+      tiles[i++] = make_int4(g, start + r, n, 0);
+    }
+  }
+}
+
 // ------------------------------------------------------ LDS ring helpers
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -138,6 +169,7 @@ struct DispatchExtras {
   int32_t* tile_count;
   int BM, has_shared;
   int balanced;           // near-equal tiles (multiples of 16 rows)
+  int tallBM;             // > 0: groups of more than BM rows in tall tiles
 };
 bool dispatch_small_ok(int T, int E, int L, int P);
 hipError_t launch_dispatch_small(const DispatchArgs& a, const DispatchExtras& x,
@@ -205,14 +237,16 @@ hipError_t launch_ffn_fp8(FfnArgs& a, hipStream_t s);
 // rows per tile the FFN uses for this recipe and expected group size; sets
 // *balanced when a group's tiles are near-equal multiples of 16 rows
 int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int I, int* balanced);
+// rows of the tall tiles that groups larger than a tile get (0: none)
+int ffn_tall_rows(int act, int wdt, int BM);
 int ffn_fp8_tile_rows(int rows_hint, int H, int I, int* balanced);
 // gate/up LDS-ring GEMM over a list of tiles of up to gemm_tile_rows() rows
 hipError_t launch_gemm_bf16_gateup(const FfnArgs& f, hipStream_t s);
 hipError_t launch_gemm_bf16_down(const FfnArgs& f, hipStream_t s);
 int gemm_tile_rows();
 hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
-                              int T, int BM, int balanced, int4* tiles,
-                              int32_t* count, hipStream_t s);
+                              int T, int BM, int balanced, int tallBM,
+                              int4* tiles, int32_t* count, hipStream_t s);
 
 // a K x N matrix stored KN or NK -> its prepared form for `dtype` (float32
 // [K][N]; bf16 16x32 or fp8 16x128 packed operand blocks)

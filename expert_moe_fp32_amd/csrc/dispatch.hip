@@ -143,8 +143,8 @@ __device__ void tile_list_from_offsets(const int32_t* off, int P, int T,
       int nt = 0;
       if (g < G) {
         const int rows = g < P ? off[g + 1] - off[g] : T;
-        int per;
-        nt = tile_split(rows, x.BM, x.balanced, &per);
+        int per, tall;
+        nt = group_tiles(rows, x.BM, x.balanced, x.tallBM, &per, &tall);
       }
       int tot;
       const int ex = wave_excl_scan(nt, &tot);
@@ -161,11 +161,9 @@ __device__ void tile_list_from_offsets(const int32_t* off, int P, int T,
     const int start = g < P ? off[g] : 0;
     const int rows = g < P ? off[g + 1] - start : T;
     if (rows == 0) continue;
-    int per;
-    tile_split(rows, x.BM, x.balanced, &per);
-    int i = tb[g];
-    for (int r = 0; r < rows; r += per, ++i)
-      x.tiles[i] = make_int4(g, start + r, min(per, rows - r), 0);
+    int per, tall;
+    group_tiles(rows, x.BM, x.balanced, x.tallBM, &per, &tall);
+    write_group_tiles(x.tiles, tb[g], g, start, rows, per, tall);
   }
 }
 

@@ -36,6 +36,8 @@
 // MFMA operand convention (16x16x32 bf16): lane l supplies row (A) or column
 // (B) l % 16 and the 8 K-values of K-slot l / 16; the accumulator of lane l
 // holds rows 4 * (l / 16) + i, i < 4, of column l % 16.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -69,14 +71,15 @@ struct KArgs {
 // tiles of BM2 rows, each with its count.
 __global__ __launch_bounds__(1024) void k_build_tiles(
     const int32_t* __restrict__ offsets, int P, int has_shared, int T, int BM,
-    int balanced, int4* __restrict__ tiles, int32_t* __restrict__ count,
-    int BM2, int4* __restrict__ tiles2, int32_t* __restrict__ count2) {
+    int balanced, int tallBM, int4* __restrict__ tiles,
+    int32_t* __restrict__ count, int BM2, int4* __restrict__ tiles2,
+    int32_t* __restrict__ count2) {
   __shared__ int32_t base[2][MOE_LMAX + 2];
   const int G = P + (has_shared ? 1 : 0);
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
     const int rows = g < P ? offsets[g + 1] - offsets[g] : T;
-    int per;
-    base[0][g + 1] = tile_split(rows, BM, balanced, &per);
+    int per, tall;
+    base[0][g + 1] = group_tiles(rows, BM, balanced, tallBM, &per, &tall);
     base[1][g + 1] = (rows + BM2 - 1) / BM2;
   }
   __syncthreads();
@@ -91,13 +94,11 @@ __global__ __launch_bounds__(1024) void k_build_tiles(
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
     const int start = g < P ? offsets[g] : 0;
     const int rows = g < P ? offsets[g + 1] - start : T;
-    int per;
-    tile_split(rows, BM, balanced, &per);
-    int i = base[0][g];
-    for (int r = 0; r < rows; r += per, ++i)
-      tiles[i] = make_int4(g, start + r, min(per, rows - r), 0);
+    int per, tall;
+    group_tiles(rows, BM, balanced, tallBM, &per, &tall);
+    write_group_tiles(tiles, base[0][g], g, start, rows, per, tall);
     if (tiles2) {
-      i = base[1][g];
+      int i = base[1][g];
       for (int r = 0; r < rows; r += BM2, ++i)
         tiles2[i] = make_int4(g, start + r, min(BM2, rows - r), 0);
     }
@@ -152,6 +153,16 @@ __device__ __forceinline__ void store_block(const KArgs& a, bool sh, int row0,
 // outputs an item), so every wavefront keeps two weight streams in flight.
 // A tile has up to 16*NMB rows.  K chunk = 128 (4 MFMA steps), prefetched
 // one chunk ahead.
+//
+// A group larger than one tile (a hot expert in a decode batch) is cut into
+// tall tiles of up to 4 * 16 * NMB rows instead, each listed four times
+// (descriptor mark 1 + Q, Q = 0..3): item (quarter Q, nb) has all four
+// wavefronts stream the same two weight columns -- gate and up of block
+// nb*4 + Q, or down blocks nb*8 + Q and nb*8 + Q + 4 -- each for its own 16
+// * NMB rows of the tile.  The four identical streams go through the caches
+// (ordinary loads: the first miss fetches, the others hit), so a hot
+// expert's weights come from memory once per tall tile rather than once per
+// 16 * NMB rows; small tiles keep the non-temporal stream.
 template <int MODE, int NMB>
 __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -162,9 +173,13 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
     const int tile = item / a.nb_per_tile;
     const int nb = item - tile * a.nb_per_tile;
     const int4 td = a.tiles[tile];
-    const int g = td.x, row0 = td.y, nrows = td.z;
+    const int g = td.x;
     const bool sh = g == a.P;
-    const int nb16 = MODE == MODE_GATEUP ? nb * 4 + wv : nb * 8 + wv;
+    const int quarter = td.w;                    // 0: an ordinary tile
+    const int wcol = quarter ? quarter - 1 : wv; // the wave's column block
+    const int wrow = quarter ? 16 * NMB * wv : 0;  // and first tile row
+    const int row0 = td.y + wrow, nrows = td.z - wrow;   // this wave's rows
+    const int nb16 = MODE == MODE_GATEUP ? nb * 4 + wcol : nb * 8 + wcol;
     const u32x4_t* b0p = (const u32x4_t*)(sh ? a.w0_sh : a.w0_arr[g]) +
                          (size_t)nb16 * KB * 64 + lane;
     const u32x4_t* b1p =
@@ -179,7 +194,8 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
       av[mb] = r < nrows;
       ap[mb] = a_row(a, sh, row0 + (av[mb] ? r : 0)) + 8 * q;
     }
-    const int nmb = (nrows + 15) >> 4;   // active row blocks (uniform)
+    // active row blocks of this wave (uniform; none past a tall tile's end)
+    const int nmb = nrows <= 0 ? 0 : min((nrows + 15) >> 4, NMB);
     f32x4_t acc0[NMB], acc1[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
@@ -187,49 +203,62 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
       acc1[mb] = acc0[mb];
     }
     const u32x4_t zero = {0u, 0u, 0u, 0u};
-    u32x4_t b0c[4], b1c[4], acur[NMB][4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      b0c[s] = load_nt(b0p + s * 64);
-      b1c[s] = load_nt(b1p + s * 64);
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-        acur[mb][s] = av[mb] ? *(const u32x4_t*)(ap[mb] + 32 * s) : zero;
-    }
-    for (int k0 = 0; k0 < K; k0 += 128) {
-      u32x4_t b0n[4], b1n[4], anext[NMB][4];
-      const bool more = k0 + 128 < K;
-      if (more) {
-        const int kb = (k0 + 128) / 32;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          b0n[s] = load_nt(b0p + (kb + s) * 64);
-          b1n[s] = load_nt(b1p + (kb + s) * 64);
-#pragma unroll
-          for (int mb = 0; mb < NMB; ++mb)
-            anext[mb][s] = av[mb] ? *(const u32x4_t*)(ap[mb] + k0 + 128 + 32 * s) : zero;
-        }
-      }
+    // A quarter wavefront without rows streams nothing but keeps the
+    // quarter's per-chunk barriers, which hold the four streams together so
+    // the caches see one request at a time.
+    const bool active = nmb > 0;
+    auto k_loop = [&](auto nt_c) {
+      constexpr bool NT = decltype(nt_c)::value;
+      auto wload = [&](const u32x4_t* p) -> u32x4_t {
+        return NT ? load_nt(p) : (active ? *p : zero);
+      };
+      u32x4_t b0c[4], b1c[4], acur[NMB][4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        b0c[s] = wload(b0p + s * 64);
+        b1c[s] = wload(b1p + s * 64);
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          if (mb < nmb) {
-            acc0[mb] = mfma16(acur[mb][s], b0c[s], acc0[mb]);
-            acc1[mb] = mfma16(acur[mb][s], b1c[s], acc1[mb]);
+        for (int mb = 0; mb < NMB; ++mb)
+          acur[mb][s] = av[mb] ? *(const u32x4_t*)(ap[mb] + 32 * s) : zero;
+      }
+      for (int k0 = 0; k0 < K; k0 += 128) {
+        u32x4_t b0n[4], b1n[4], anext[NMB][4];
+        const bool more = k0 + 128 < K;
+        if (!NT) __syncthreads();                // the quarter's four streams
+        if (more) {
+          const int kb = (k0 + 128) / 32;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            b0n[s] = wload(b0p + (kb + s) * 64);
+            b1n[s] = wload(b1p + (kb + s) * 64);
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+              anext[mb][s] = av[mb] ? *(const u32x4_t*)(ap[mb] + k0 + 128 + 32 * s) : zero;
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) {
+            if (mb < nmb) {
+              acc0[mb] = mfma16(acur[mb][s], b0c[s], acc0[mb]);
+              acc1[mb] = mfma16(acur[mb][s], b1c[s], acc1[mb]);
+            }
+          }
+        }
+        if (more) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            b0c[s] = b0n[s];
+            b1c[s] = b1n[s];
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) acur[mb][s] = anext[mb][s];
           }
         }
       }
-      if (more) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          b0c[s] = b0n[s];
-          b1c[s] = b1n[s];
-#pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) acur[mb][s] = anext[mb][s];
-        }
-      }
-    }
+    };
+    if (quarter) k_loop(std::integral_constant<bool, false>{});
+    else k_loop(std::integral_constant<bool, true>{});
     const int n = nb16 * 16 + c16;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
@@ -468,11 +497,18 @@ int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int I, int* balanced) 
 }
 
 hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
-                              int T, int BM, int balanced, int4* tiles,
-                              int32_t* count, hipStream_t s) {
+                              int T, int BM, int balanced, int tallBM,
+                              int4* tiles, int32_t* count, hipStream_t s) {
   k_build_tiles<<<1, 1024, 0, s>>>(offsets, P, has_shared, T, BM, balanced,
-                                   tiles, count, BM, nullptr, nullptr);
+                                   tallBM, tiles, count, BM, nullptr, nullptr);
   return hipGetLastError();
+}
+
+// bf16 streaming: groups beyond one 32-row tile get tall tiles of 4 x 32
+// rows (listed as four quarters)
+static constexpr int kTallRows = 128;
+int ffn_tall_rows(int act, int wdt, int BM) {
+  return (act == MOE_BF16 && wdt == MOE_BF16 && BM == 32) ? kTallRows : 0;
 }
 
 hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
@@ -490,14 +526,15 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   // down runs the 128 x 128 tile kernel (H not a multiple of 256); a list
   // already written by the dispatch is the first one
   const bool down_list = ring && f.H % 256 != 0;
+  const int tallBM = ffn_tall_rows(f.act, f.wdt, BM);
   if (!f.tiles_ready)
     k_build_tiles<<<1, 1024, 0, s>>>(f.offsets, f.P, f.has_shared, f.T, BM,
-                                     balanced, f.tiles, f.tile_count, TBM,
-                                     down_list ? f.tiles_down : nullptr,
+                                     balanced, tallBM, f.tiles, f.tile_count,
+                                     TBM, down_list ? f.tiles_down : nullptr,
                                      f.tile_count + 1);
   else if (down_list)
     k_build_tiles<<<1, 1024, 0, s>>>(f.offsets, f.P, f.has_shared, f.T, TBM, 0,
-                                     f.tiles_down, f.tile_count + 1, TBM,
+                                     0, f.tiles_down, f.tile_count + 1, TBM,
                                      nullptr, nullptr);
   if (f.events) hipEventRecord(f.events[0], s);
   // bound on the tile count for the grid size

@@ -876,7 +876,7 @@ hipError_t launch_ffn_fp8(FfnArgs& f, hipStream_t s) {
   const int BM = ffn_fp8_tile_rows(f.rows_hint, f.H, f.I, &balanced);
   const bool stream = balanced != 0;
   if (!f.tiles_ready)
-    launch_build_tiles(f.offsets, f.P, f.has_shared, f.T, BM, balanced,
+    launch_build_tiles(f.offsets, f.P, f.has_shared, f.T, BM, balanced, 0,
                        f.tiles, f.tile_count, s);
   if (f.events) hipEventRecord(f.events[0], s);
   const long hrows = (long)f.cap + (f.has_shared ? f.T : 0);

@@ -139,6 +139,24 @@ def test_full_decode_all_tokens(out_fmt):
     print(f"  max|err|/RMS = {r:.3e}")
 
 
+def test_full_decode_skewed_all_tokens():
+    """A decode batch with the Zipf logit bias (one local expert holds
+    several times the mean rows: its rows run as tall tiles whose four
+    quarters share one weight stream), every token, float32 output against
+    the raw bar."""
+    wl = make_workload("decode_skewed", seed=0, out="f32")
+    print(f"layer {wl.describe()}", flush=True)
+    out, counts = run_layer(wl)
+    local = counts[wl.expert_begin: wl.expert_begin + wl.num_local]
+    assert local.max() > 32 and local.max() > 4 * local.mean()
+    ref = oracle_out(wl, workers=16)
+    assert np.array_equal(counts, ref.counts)
+    r = check_output(out, ref.out, wl.out, BARS["bf16"], "decode_skewed",
+                     literal=True)
+    print(f"  busiest {local.max()} rows, mean {local.mean():.1f}; "
+          f"max|err|/RMS = {r:.3e}")
+
+
 @pytest.fixture(scope="module")
 def skewed():
     return make_workload("skewed", seed=0)
