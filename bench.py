@@ -56,14 +56,60 @@ WORKLOADS = ["tiny", "decode", "decode_skewed", "prefill", "skewed",
 
 
 # Counter figures per launch of each workload's dominant (gate/up) kernel,
-# from rocprofv3 --pmc runs of this script (profiles/ has the commands and
-# tables).  HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
-# scaled by the factor that makes the same counter read the known size of
-# the weight-prepack kernel in the same run.  MFMA utilisation:
-# SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 1024 SIMDs.  The figures
-# hold for the kernel source they were taken on: when the SHA-256 of its
-# files differs, they are reported as null.
-COUNTERS = {}
+# from rocprofv3 --pmc runs of this script (the profile named in each entry
+# has the commands and the per-kernel tables).  HBM bytes: FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes the
+# same counter read the known size of a streaming kernel with the same
+# 16-byte accesses in the same run (bf16: the weight prepack k_pack_bf16;
+# FP8: the activation quantiser k_quant_rows_fp8).  MFMA utilisation:
+# SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8 (the counter sums the 8
+# XCDs) x 1024 SIMDs, i.e. the fraction of the kernel's own cycles the
+# matrix cores were busy.  The figures hold for the kernel source they were
+# taken on: when the SHA-256 of its files differs, they are reported as null.
+COUNTERS = {
+    "decode": {
+        "kernel": "k_stream_bf16<0, 2>", "profile": "profiles/layer_stream_bf16_decode.md",
+        "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
+        "sha": "76bdc431fd67f56c",
+        "fetch_kib": 794476.9, "fetch_factor": 1.9976,
+        "write_kib": 988.9, "write_factor": 1.0,
+        "mfma_util": 0.051},
+    "decode_skewed": {
+        "kernel": "k_stream_bf16<0, 2>", "profile": "profiles/layer_stream_bf16_decode_skewed.md",
+        "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
+        "sha": "76bdc431fd67f56c",
+        "fetch_kib": 207739.0, "fetch_factor": 1.9976,
+        "write_kib": 876.9, "write_factor": 1.0,
+        "mfma_util": 0.052},
+    "prefill": {
+        "kernel": "k_gemm_bf16<0, 4, 2, 2, 4>", "profile": "profiles/layer_gemm_bf16_prefill.md",
+        "files": ["expert_moe_fp32_amd/csrc/gemm_bf16.hip", "expert_moe_fp32_amd/csrc/common.h"],
+        "sha": "10019f9cf7e4ee98",
+        "fetch_kib": 1949412.5, "fetch_factor": 1.998,
+        "write_kib": 65704.0, "write_factor": 1.0,
+        "mfma_util": 0.608},
+    "skewed_eplb": {
+        "kernel": "k_gemm_bf16<0, 4, 2, 2, 4>", "profile": "profiles/layer_gemm_bf16_skewed_eplb.md",
+        "files": ["expert_moe_fp32_amd/csrc/gemm_bf16.hip", "expert_moe_fp32_amd/csrc/common.h"],
+        "sha": "10019f9cf7e4ee98",
+        "fetch_kib": 2055599.2, "fetch_factor": 1.9979,
+        "write_kib": 50612.0, "write_factor": 1.0,
+        "mfma_util": 0.429},
+    "fp8": {
+        "kernel": "k_ring_fp8<0, 10>", "profile": "profiles/layer_ring_fp8_fp8.md",
+        "files": ["expert_moe_fp32_amd/csrc/ffn_fp8.hip", "expert_moe_fp32_amd/csrc/common.h"],
+        "sha": "9610ca217221f29a",
+        "fetch_kib": 485389.2, "fetch_factor": 1.9991,
+        "write_kib": 33232.1, "write_factor": 1.0,
+        "mfma_util": 0.299},
+    "lowlat": {
+        "kernel": "k_wstream_fp8<0, 2>", "profile": "profiles/layer_wstream_fp8_lowlat.md",
+        "files": ["expert_moe_fp32_amd/csrc/ffn_fp8.hip", "expert_moe_fp32_amd/csrc/common.h"],
+        "sha": "9610ca217221f29a",
+        "fetch_kib": 452620.3, "fetch_factor": 1.9723,
+        "write_kib": 278.1, "write_factor": 1.0,
+        "mfma_util": 0.079},
+}
 
 
 def _source_sha(files):
@@ -346,13 +392,14 @@ def measure(bn: Bench, steps, warmup, graph=False):
                     peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic,
                     algorithmic_bytes=int(u["gu_bytes"]),
-                    avg_us=round(gu_s * 1e6, 2))
+                    avg_us=round(gu_s * 1e6, 2), mfma_util=mfma_util)
     else:
         achieved = u["gu_flops"] / gu_s / 1e12
         roof = dict(bound="mfma", kernel="gate_up", achieved=round(achieved, 1),
                     peak=peak_tf, unit="TFLOP/s",
                     frac=round(achieved / peak_tf, 4), traffic=traffic,
                     algorithmic_flops=u["gu_flops"],
+                    algorithmic_bytes=int(u["gu_bytes"]),
                     avg_us=round(gu_s * 1e6, 2), mfma_util=mfma_util)
     # whole-layer roofline: the larger of the flop time at the MFMA peak and
     # the time to move the minimum bytes (weights of non-empty experts, x,

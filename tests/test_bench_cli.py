@@ -19,13 +19,16 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 def test_counter_table_names_existing_kernel_sources():
     # every counter entry points at source files that exist, so its SHA-256
-    # gate can be evaluated, and names a workload the benchmark runs
+    # gate can be evaluated, at the profile its figures come from, and names
+    # a workload the benchmark runs
     sys.path.insert(0, ROOT)
     import bench
     for wl, t in bench.COUNTERS.items():
         assert wl in bench.WORKLOADS
         for f in t["files"]:
             assert os.path.exists(os.path.join(ROOT, f)), (wl, f)
+        if "profile" in t:
+            assert os.path.exists(os.path.join(ROOT, t["profile"])), (wl, t["profile"])
         if "fetch_kib" in t:
             assert t["fetch_factor"] > 0 and t["write_factor"] > 0
         if "mfma_util" in t:
