@@ -149,8 +149,10 @@ __device__ __forceinline__ void store_block(const KArgs& a, bool sh, int row0,
 // ---------------------------------------------- weight-streaming kernel
 // Workgroup = 4 wavefronts; wavefront w streams two packed row blocks (16
 // channels each) over the whole reduction: gate and up of block nb*4 + w
-// (64 outputs an item), or down blocks nb*8 + w and nb*8 + w + 4 (128
-// outputs an item), so every wavefront keeps two weight streams in flight.
+// (64 outputs an item), or the neighbouring down blocks nb*8 + 2w and
+// nb*8 + 2w + 1 (128 outputs an item; their runs lie 64 KiB apart, and the
+// decode down pass ran 138 -> 133 us against blocks 64 channels apart), so
+// every wavefront keeps two weight streams in flight.
 // A tile has up to 16*NMB rows.  K chunk = 128 (4 MFMA steps), prefetched
 // one chunk ahead.
 //
@@ -158,7 +160,7 @@ __device__ __forceinline__ void store_block(const KArgs& a, bool sh, int row0,
 // tall tiles of up to 4 * 16 * NMB rows instead, each listed four times
 // (descriptor mark 1 + Q, Q = 0..3): item (quarter Q, nb) has all four
 // wavefronts stream the same two weight columns -- gate and up of block
-// nb*4 + Q, or down blocks nb*8 + Q and nb*8 + Q + 4 -- each for its own 16
+// nb*4 + Q, or down blocks nb*8 + 2Q and nb*8 + 2Q + 1 -- each for its own 16
 // * NMB rows of the tile.  The four identical streams go through the caches
 // (ordinary loads: the first miss fetches, the others hit), so a hot
 // expert's weights come from memory once per tall tile rather than once per
@@ -179,13 +181,13 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
     const int wcol = quarter ? quarter - 1 : wv; // the wave's column block
     const int wrow = quarter ? 16 * NMB * wv : 0;  // and first tile row
     const int row0 = td.y + wrow, nrows = td.z - wrow;   // this wave's rows
-    const int nb16 = MODE == MODE_GATEUP ? nb * 4 + wcol : nb * 8 + wcol;
+    const int nb16 = MODE == MODE_GATEUP ? nb * 4 + wcol : nb * 8 + 2 * wcol;
     const u32x4_t* b0p = (const u32x4_t*)(sh ? a.w0_sh : a.w0_arr[g]) +
                          (size_t)nb16 * KB * 64 + lane;
     const u32x4_t* b1p =
         MODE == MODE_GATEUP
             ? (const u32x4_t*)(sh ? a.w1_sh : a.w1_arr[g]) + (size_t)nb16 * KB * 64 + lane
-            : b0p + (size_t)4 * KB * 64;        // down: the block 64 channels on
+            : b0p + (size_t)KB * 64;            // down: the next block
     const bf16_t* ap[NMB];
     bool av[NMB];
 #pragma unroll
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
       if (mb >= nmb) continue;
       store_block<MODE>(a, sh, row0, nrows, mb * 16, n, acc0[mb], acc1[mb]);
       if (MODE == MODE_DOWN)
-        store_block<MODE>(a, sh, row0, nrows, mb * 16, n + 64, acc1[mb], acc1[mb]);
+        store_block<MODE>(a, sh, row0, nrows, mb * 16, n + 16, acc1[mb], acc1[mb]);
     }
   }
 }
@@ -596,7 +598,7 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
     long grid = items < cu * 4 ? items : cu * 4;
     k_f32<MODE_DOWN><<<(unsigned)grid, 256, 0, s>>>(a);
   } else if (stream) {
-    a.nb_per_tile = a.N / 128;                // two 64-apart blocks per wave
+    a.nb_per_tile = a.N / 128;                // two neighbouring blocks per wave
     long items = max_tiles * a.nb_per_tile;
     // persistent: the two workgroups a CU holds at this kernel's registers
     long grid = items < cu * 2 ? items : cu * 2;
