@@ -233,3 +233,11 @@ def fp8_complete_check(wl, tokens=None, layout="kn", workers=0):
     st = check_fp8_complete(wl, got, ref, tokens)
     print(f"  {st}", flush=True)
     return st
+
+
+def sample_tokens(T, n, seed=0):
+    """n distinct seeded token indices, plus the first and the last."""
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    s |= {0, T - 1}
+    return np.array(sorted(s))

@@ -73,6 +73,15 @@ def check_against_oracle(wl, got, l2p=None, rep=None, P=None):
     ("decode", {}),
     ("prefill", dict(H=256, I=128)),
     ("fp8", dict(H=512, I=128)),
+    # more than 256 local experts: the multi-block path's per-expert ballot
+    # loop, with many blocks (T = 2000) and with one (T = 700)
+    ("tiny", dict(T=2000, E=512, num_local=300, expert_begin=100, k=8, H=64,
+                  I=64)),
+    ("tiny", dict(T=700, E=512, num_local=300, expert_begin=0, k=8, H=64,
+                  I=64)),
+    # the largest share: 1024 local experts, k = 16
+    ("tiny", dict(T=500, E=1024, num_local=1024, expert_begin=0, k=16, H=64,
+                  I=64)),
 ])
 def test_dispatch_matches_oracle(name, kw):
     wl = make_workload(name, seed=0, **kw)

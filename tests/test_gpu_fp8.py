@@ -129,6 +129,17 @@ def test_fp8_full_all_tokens():
     assert st["codes"] > 4000 * 2048
 
 
+def test_fp8_many_rows_per_expert_sampled():
+    """FP8 prefill with 8,192 tokens: about 256 rows per local expert, more
+    than one 160-row tile holds, so gate/up and down run the 128 x 128 tiled
+    kernel and h goes through the separate quantisation pass; 256 sampled
+    tokens at full size (H = 7168, I = 2048)."""
+    from .helpers import sample_tokens
+    wl = make_workload("fp8", seed=2, T=8192)
+    st = complete_check(wl, tokens=sample_tokens(wl.T, 256), workers=16)
+    assert st["codes"] > 200 * 2048          # about one local pair a token
+
+
 def test_matrix_instruction_block_error_within_the_model():
     """The oracle's error model of an FP8 block sum (oracle.moe.C_BLOCK: a
     128-product sum returned with an error of RMS at most C_BLOCK u sum|p|),

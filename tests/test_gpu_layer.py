@@ -11,7 +11,8 @@ from oracle import eplb, moe as omoe
 from synth import make_workload
 
 from .helpers import (BARS, check_output, device_layer, fp8_complete_check,
-                      out_to_f64, phys_to_logical_from_map, recipe)
+                      out_to_f64, phys_to_logical_from_map, recipe,
+                      sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,13 +47,6 @@ def oracle_out(wl, tokens=None, l2p=None, rep=None, P=None, workers=0):
     res = omoe.layer_from_workload(wl, ex, l2p=l2p, rep_count=rep, P=P,
                                    token_subset=tokens, workers=workers)
     return res
-
-
-def sample_tokens(T, n, seed=0):
-    rng = np.random.default_rng(seed)
-    s = set(rng.choice(T, size=min(n, T), replace=False).tolist())
-    s |= {0, T - 1}
-    return np.array(sorted(s))
 
 
 @pytest.mark.parametrize("name,kw", [
