@@ -165,7 +165,8 @@ moe_status dispatch_impl(const moe_problem* p, const void* x,
                          int32_t* pair_row, const DispatchScratch& d,
                          hipStream_t s, hipEvent_t ev_index = nullptr,
                          bool materialize = true,
-                         const DispatchExtras* extras = nullptr) {
+                         const DispatchExtras* extras = nullptr,
+                         bool x_quantised = false) {
   DispatchArgs a{};
   a.T = p->T;
   a.k = p->k;
@@ -198,7 +199,8 @@ moe_status dispatch_impl(const moe_problem* p, const void* x,
   const int cap = (int)cap_rows(p);
   const int32_t* nrows = offsets + p->num_physical;
   if (p->weight_dtype == MOE_FP8_E4M3) {
-    e = launch_quant_rows_fp8((const bf16_t*)x, p->T, p->H, d.xq, d.xs, s);
+    if (!x_quantised)     // else done with the router (launch_route_quant_fp8)
+      e = launch_quant_rows_fp8((const bf16_t*)x, p->T, p->H, d.xq, d.xs, s);
     if (e != hipSuccess || !materialize) return hip_status(e);
     e = launch_gather_rows(d.xq, (size_t)p->H, row_token, nrows, cap, x_perm, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -483,14 +485,22 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
                             p->H, p->I, &extras.balanced);
   extras.tallBM = ffn_tall_rows(p->act_dtype, p->weight_dtype, extras.BM);
   extras.has_shared = p->has_shared;
-  if (launch_route_topk(logits, bias, p->T, p->E, p->k, L.ids, L.tw,
-                        nullptr, s) != hipSuccess)
-    return MOE_ERR_HIP;
+  // FP8 recipe: the router and the activation quantiser share one launch
+  // (the quantiser reads only x), so the router's latency hides under the
+  // quantiser's stream; the route stage then holds both.
+  const bool fp8_q = p->weight_dtype == MOE_FP8_E4M3 && p->E <= 256;
+  const hipError_t re =
+      fp8_q ? launch_route_quant_fp8(logits, bias, p->T, p->E, p->k, L.ids,
+                                     L.tw, (const bf16_t*)x, p->H, L.d.xq,
+                                     L.d.xs, s)
+            : launch_route_topk(logits, bias, p->T, p->E, p->k, L.ids, L.tw,
+                                nullptr, s);
+  if (re != hipSuccess) return MOE_ERR_HIP;
   if (ev) hipEventRecord(ev[1], s);
   st = dispatch_impl(p, x, L.ids, L.tw, l2p, replica_count, L.x_perm,
                      L.x_perm_scales, L.offsets, L.row_token, L.row_weight,
                      L.pair_row, L.d, s, ev ? ev[2] : nullptr,
-                     /*materialize=*/false, &extras);
+                     /*materialize=*/false, &extras, /*x_quantised=*/fp8_q);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[3], s);
   // The expert kernels read each routed row straight from the token rows

@@ -172,6 +172,12 @@ struct DispatchExtras {
   int tallBM;             // > 0: groups of more than BM rows in tall tiles
 };
 bool dispatch_small_ok(int T, int E, int L, int P);
+// FP8 layer: router top-k (E <= 256) and the activation quantiser in one
+// launch (codes [T][H], scales [T][H/128])
+hipError_t launch_route_quant_fp8(const float* logits, const float* bias,
+                                  int T, int E, int k, int32_t* ids, float* w,
+                                  const bf16_t* x, int H, uint8_t* codes,
+                                  float* scales, hipStream_t s);
 hipError_t launch_dispatch_small(const DispatchArgs& a, const DispatchExtras& x,
                                  hipStream_t s);
 // multi-block dispatch index; x.tiles (optional) receives the FFN tile list

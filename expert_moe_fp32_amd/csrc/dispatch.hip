@@ -16,7 +16,7 @@
 //      (offsets).
 //   3. k_permute: the ballots again give each pair its rank inside the
 //      wavefront; block base + earlier wavefronts + that rank is n.
-#include "common.h"
+#include "route_row.h"
 
 namespace moe {
 
@@ -475,11 +475,10 @@ hipError_t launch_gather_rows_words(const void* x, int row_words,
 }
 
 // ----------------------------------------------------- FP8 quantisation
-// One wavefront per (token, 128-channel group): amax over the group, scale
-// amax/448 (1 if amax = 0), codes RNE(fl32(x / scale)) saturated.
-// Per-token, per-128-channel E4M3 quantisation: a lane takes 8 consecutive
-// channels (one 16-byte load), the 16 lanes of a DPP row one 128-channel
-// group, whose amax is a 4-step row rotation.
+// Per-token, per-128-channel E4M3 quantisation: amax over the group, scale
+// amax/448 (1 if amax = 0), codes RNE(fl32(x / scale)) saturated.  A lane
+// takes 8 consecutive channels (one 16-byte load), the 16 lanes of a DPP row
+// one 128-channel group, whose amax is a 4-step row rotation.
 __device__ __forceinline__ float row_max_f32(float v) {
 #define ROWF(ctrl)                                                            \
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(                    \
@@ -489,10 +488,11 @@ __device__ __forceinline__ float row_max_f32(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(256) void k_quant_rows_fp8(
-    const bf16_t* __restrict__ x, long n8, uint8_t* __restrict__ codes,
-    float* __restrict__ scales) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;   // chunk of 8 values
+// Chunk i (8 values) of the row-major activation rows; n8 chunks in all.
+__device__ __forceinline__ void quant_chunk_fp8(const bf16_t* __restrict__ x,
+                                                long i, long n8,
+                                                uint8_t* __restrict__ codes,
+                                                float* __restrict__ scales) {
   const bool valid = i < n8;               // whole rows of 16 lanes agree
   u32x4_t raw = {0u, 0u, 0u, 0u};
   if (valid) raw = *(const u32x4_t*)(x + 8 * i);
@@ -516,6 +516,48 @@ __global__ __launch_bounds__(256) void k_quant_rows_fp8(
   if (!valid) return;
   *(uint2*)(codes + 8 * i) = make_uint2(lo, hi);
   if ((threadIdx.x & 15) == 0) scales[i >> 4] = sc;
+}
+
+__global__ __launch_bounds__(256) void k_quant_rows_fp8(
+    const bf16_t* __restrict__ x, long n8, uint8_t* __restrict__ codes,
+    float* __restrict__ scales) {
+  quant_chunk_fp8(x, (long)blockIdx.x * 256 + threadIdx.x, n8, codes, scales);
+}
+
+// The FP8 layer's router and activation quantiser in one launch: the first
+// nroute workgroups route 16 tokens each (route_row.h), the rest quantise,
+// so the router's latency hides under the quantiser's stream instead of
+// preceding it (the two read different inputs and write different outputs).
+template <int KPL, bool BIAS>
+__global__ __launch_bounds__(256) void k_route_quant_fp8(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T,
+    int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
+    int nroute, const bf16_t* __restrict__ x, long n8,
+    uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  if ((int)blockIdx.x < nroute)
+    route_rows_block<KPL, BIAS>(logits, bias, T, E, k, ids, w, blockIdx.x);
+  else
+    quant_chunk_fp8(x, (long)(blockIdx.x - nroute) * 256 + threadIdx.x, n8,
+                    codes, scales);
+}
+
+hipError_t launch_route_quant_fp8(const float* logits, const float* bias,
+                                  int T, int E, int k, int32_t* ids, float* w,
+                                  const bf16_t* x, int H, uint8_t* codes,
+                                  float* scales, hipStream_t s) {
+  const int nroute = (T + 15) / 16;
+  const long n8 = (long)T * H / 8;          // H % 128 == 0
+  const unsigned grid = (unsigned)(nroute + (n8 + 255) / 256);
+#define ROUTE_QUANT(KPL)                                                      \
+  (bias ? k_route_quant_fp8<KPL, true><<<grid, 256, 0, s>>>(logits, bias, T, E, k, ids, w, nroute, x, n8, codes, scales) \
+        : k_route_quant_fp8<KPL, false><<<grid, 256, 0, s>>>(logits, bias, T, E, k, ids, w, nroute, x, n8, codes, scales))
+  if (E <= 16) ROUTE_QUANT(1);
+  else if (E <= 32) ROUTE_QUANT(2);
+  else if (E <= 64) ROUTE_QUANT(4);
+  else if (E <= 128) ROUTE_QUANT(8);
+  else ROUTE_QUANT(16);
+#undef ROUTE_QUANT
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_rows_fp8(const bf16_t* x, int T, int H,
