@@ -150,9 +150,10 @@ __device__ __forceinline__ void store_block(const KArgs& a, bool sh, int row0,
 // Workgroup = 4 wavefronts; wavefront w streams two packed row blocks (16
 // channels each) over the whole reduction: gate and up of block nb*4 + w
 // (64 outputs an item), or the neighbouring down blocks nb*8 + 2w and
-// nb*8 + 2w + 1 (128 outputs an item; their runs lie 64 KiB apart, and the
-// decode down pass ran 138 -> 133 us against blocks 64 channels apart), so
-// every wavefront keeps two weight streams in flight.
+// nb*8 + 2w + 1 (128 outputs an item; adjacent runs, and each row's two
+// 16-float output blocks fill one 128-byte line -- the decode down pass ran
+// 138 -> 133 us against blocks 64 channels apart), so every wavefront keeps
+// two weight streams in flight.
 // A tile has up to 16*NMB rows.  K chunk = 128 (4 MFMA steps), prefetched
 // one chunk ahead.
 //
