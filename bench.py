@@ -70,56 +70,56 @@ COUNTERS = {
     "tiny": {
         "kernel": "k_f32<0>", "profile": "profiles/layer_f32_tiny.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "76bdc431fd67f56c",
-        "fetch_kib": 1333.0, "fetch_factor": 1.5784,
+        "sha": "35f656de498adb24",
+        "fetch_kib": 1333.0, "fetch_factor": 1.5785,
         "write_kib": 128.0, "write_factor": 1.0},
     "decode": {
         "kernel": "k_stream_bf16<0, 2>", "profile": "profiles/layer_stream_bf16_decode.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "76bdc431fd67f56c",
-        "fetch_kib": 794476.9, "fetch_factor": 1.9976,
+        "sha": "35f656de498adb24",
+        "fetch_kib": 794480.7, "fetch_factor": 1.9976,
         "write_kib": 988.9, "write_factor": 1.0,
         "mfma_util": 0.051},
     "decode_skewed": {
         "kernel": "k_stream_bf16<0, 2>", "profile": "profiles/layer_stream_bf16_decode_skewed.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "76bdc431fd67f56c",
-        "fetch_kib": 207739.0, "fetch_factor": 1.9976,
-        "write_kib": 876.9, "write_factor": 1.0,
-        "mfma_util": 0.052},
+        "sha": "35f656de498adb24",
+        "fetch_kib": 207547.2, "fetch_factor": 1.9976,
+        "write_kib": 876.2, "write_factor": 1.0,
+        "mfma_util": 0.051},
     "prefill": {
         "kernel": "k_gemm_bf16<0, 4, 2, 2, 4>", "profile": "profiles/layer_gemm_bf16_prefill.md",
         "files": ["expert_moe_fp32_amd/csrc/gemm_bf16.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "6bafd5d46fdf5259",
-        "fetch_kib": 1824114.4, "fetch_factor": 1.9979,
-        "write_kib": 71848.7, "write_factor": 1.0,
-        "mfma_util": 0.59},
+        "sha": "3abdacdc6928e143",
+        "fetch_kib": 1818199.8, "fetch_factor": 1.9979,
+        "write_kib": 71848.3, "write_factor": 1.0,
+        "mfma_util": 0.586},
     "skewed": {
         "kernel": "k_gemm_bf16<0, 4, 2, 2, 4>", "profile": "profiles/layer_gemm_bf16_skewed.md",
         "files": ["expert_moe_fp32_amd/csrc/gemm_bf16.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "6bafd5d46fdf5259",
-        "fetch_kib": 1744465.7, "fetch_factor": 1.9979,
+        "sha": "3abdacdc6928e143",
+        "fetch_kib": 1708994.9, "fetch_factor": 1.9979,
         "write_kib": 55172.0, "write_factor": 1.0,
-        "mfma_util": 0.467},
+        "mfma_util": 0.469},
     "skewed_eplb": {
         "kernel": "k_gemm_bf16<0, 4, 2, 2, 4>", "profile": "profiles/layer_gemm_bf16_skewed_eplb.md",
         "files": ["expert_moe_fp32_amd/csrc/gemm_bf16.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "6bafd5d46fdf5259",
-        "fetch_kib": 2009556.4, "fetch_factor": 1.9979,
+        "sha": "3abdacdc6928e143",
+        "fetch_kib": 1991712.3, "fetch_factor": 1.9979,
         "write_kib": 55220.1, "write_factor": 1.0,
-        "mfma_util": 0.422},
+        "mfma_util": 0.421},
     "fp8": {
         "kernel": "k_ring_fp8<0, 10>", "profile": "profiles/layer_ring_fp8_fp8.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn_fp8.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "9610ca217221f29a",
-        "fetch_kib": 485389.2, "fetch_factor": 1.9991,
+        "sha": "997ca6fdc9b5006f",
+        "fetch_kib": 485368.9, "fetch_factor": 1.9987,
         "write_kib": 33232.1, "write_factor": 1.0,
-        "mfma_util": 0.299},
+        "mfma_util": 0.295},
     "lowlat": {
         "kernel": "k_wstream_fp8<0, 2>", "profile": "profiles/layer_wstream_fp8_lowlat.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn_fp8.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "9610ca217221f29a",
-        "fetch_kib": 452620.3, "fetch_factor": 1.9723,
+        "sha": "997ca6fdc9b5006f",
+        "fetch_kib": 452611.3, "fetch_factor": 1.9594,
         "write_kib": 278.1, "write_factor": 1.0,
         "mfma_util": 0.079},
 }
