@@ -266,8 +266,13 @@ MOE_API moe_status moe_layer_forward(const moe_problem* p, const float* logits,
  * handles created by the caller; recorded in order
  *   [0] start  [1] route done  [2] dispatch index done  [3] row gather done
  *   [4] FFN tile list built  [5] gate/up done  [6] down done  [7] combine done
- * (on the T = 0 path nothing is recorded).  In the FP8 recipe the
- * quantisation of h to E4M3 falls in the down interval [5, 6]. */
+ * (on the T = 0 path nothing is recorded).  The layer writes no permuted
+ * copy of the rows (the expert kernels read token rows through the
+ * dispatch's row index), so [2, 3] holds only the FP8 activation quantiser
+ * when it runs on its own (E > 256); with E <= 256 it shares the router's
+ * launch and falls in [0, 1].  The quantisation of h to E4M3 falls in the
+ * down interval [5, 6] except where the gate/up kernel does it itself
+ * (groups of a few rows). */
 #define MOE_STAGE_EVENTS 8
 MOE_API moe_status moe_layer_forward_timed(const moe_problem* p,
                                    const float* logits, const float* bias,
