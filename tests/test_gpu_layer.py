@@ -188,6 +188,35 @@ def test_full_skewed_with_and_without_replicas(skewed):
           f"b {ref.disp.phys_counts.max() / ref.disp.phys_counts.mean():.2f}")
 
 
+@pytest.mark.parametrize("T", [96, 1200])   # streaming kernel; LDS-ring GEMM
+def test_rank_shares_sum_to_the_all_local_layer(T):
+    """Expert parallelism without a cluster: the layer run for each of 8
+    rank shares (8 of 64 experts each, expert_begin = 0, 8, ..., 56; the
+    shared expert on share 0 only), float32 outputs summed, equals the layer
+    with all 64 experts local, and both match the oracle of the all-local
+    layer under the literal bar."""
+    kw = dict(T=T, H=256, I=128, E=64, k=4, out="f32")
+    total = 0.0
+    for s in range(8):
+        wl = make_workload("prefill", seed=23, num_local=8, expert_begin=8 * s,
+                           shared=s == 0, **kw)
+        print(f"share {s}: {wl.describe()}", flush=True)
+        out, _ = run_layer(wl)
+        total = total + out
+    full = make_workload("prefill", seed=23, num_local=64, expert_begin=0,
+                         shared=True, **kw)
+    print(f"all local: {full.describe()}", flush=True)
+    out_full, _ = run_layer(full)
+    ref = oracle_out(full)
+    rms = float(np.sqrt(np.mean(ref.out ** 2)))
+    # the shares differ from the whole only in how float32 partial sums group
+    assert np.max(np.abs(total - out_full)) <= 1e-5 * rms
+    check_output(total, ref.out, "f32", BARS["bf16"], "sum of shares",
+                 literal=True)
+    check_output(out_full, ref.out, "f32", BARS["bf16"], "all local",
+                 literal=True)
+
+
 def with_hot_expert(wl, e):
     """Every token gets local expert e in its top-k (its logit raised by 20):
     one expert holds all T rows, several tiles of them."""
