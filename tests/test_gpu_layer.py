@@ -217,6 +217,35 @@ def test_rank_shares_sum_to_the_all_local_layer(T):
                  literal=True)
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("decode", dict(T=64, H=384, I=256, E=32, num_local=8, k=4)),      # stream
+    ("prefill", dict(T=600, H=256, I=256, E=16, num_local=8, k=4)),    # GEMM
+    ("fp8", dict(T=200, H=1024, I=512, E=16, num_local=8, k=4)),       # FP8 ring
+])
+def test_experts_without_rows_are_not_used(name, kw):
+    """Local experts 5, 6 and 7 get no tokens (their logits lowered by 100)
+    and NaN weights: an expert with no rows owns no tile, so nothing of it
+    reaches the output."""
+    wl = make_workload(name, seed=29, **kw)
+    logits = wl.logits.copy()
+    logits[:, wl.expert_begin + 5: wl.expert_begin + 8] -= 100.0
+    wl._cache["logits"] = logits
+    for p in (5, 6, 7):
+        w = wl.expert(p)
+        nan = np.uint16(0x7FC0) if wl.wdt == "bf16" else np.float32("nan")
+        wl._experts[p] = {key: np.full_like(v, nan) for key, v in w.items()}
+    print(f"layer {wl.describe()} (experts 5-7 empty, NaN weights)", flush=True)
+    if wl.wdt == "fp8":
+        st = fp8_complete_check(wl)
+        assert st["codes"] > 0
+        return
+    out, counts = run_layer(wl)
+    loc = counts[wl.expert_begin: wl.expert_begin + wl.num_local]
+    assert np.all(loc[5:8] == 0) and np.all(loc[:5] > 0)
+    ref = oracle_out(wl)
+    check_output(out, ref.out, wl.out, BARS[recipe(wl)], wl.describe())
+
+
 def with_hot_expert(wl, e):
     """Every token gets local expert e in its top-k (its logit raised by 20):
     one expert holds all T rows, several tiles of them."""
