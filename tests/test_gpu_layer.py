@@ -70,6 +70,10 @@ def oracle_out(wl, tokens=None, l2p=None, rep=None, P=None, workers=0):
     # transfers only): down with I = 128, gate/up with H = 128
     ("prefill", dict(T=500, H=256, I=128, E=8, num_local=8, k=2)),
     ("prefill", dict(T=500, H=128, I=256, E=8, num_local=8, k=2)),
+    # k = 1; k = E (every expert on every token); the largest k, 16 = E
+    ("decode", dict(T=64, H=384, I=256, E=32, num_local=8, k=1)),
+    ("tiny", dict(T=200, E=8, num_local=8, k=8)),
+    ("tiny", dict(T=300, E=16, num_local=16, k=16)),
 ])
 def test_layer_reduced_shapes(name, kw):
     wl = make_workload(name, seed=11, **kw)
