@@ -381,21 +381,25 @@ __global__ __launch_bounds__(256) void k_tile_bf16_down(KArgs a) {
 
 // --------------------------------------------------------- fp32 recipe
 // Float32 weights in the logical layout [K][N] (gate/up [H][I], down [I][H]).
-// A workgroup computes a 64-row x 64-output tile (both gate and up for
-// gate/up) with float32 FMAs: per 32-deep K step it stages the tile's
-// activation rows (gathered through a_rows) transposed into LDS and the
-// weight rows W[k][n0 .. n0+64) as they lie in memory, both with consecutive
-// threads on consecutive addresses; each thread then accumulates 4 rows x 4
-// outputs in registers, in ascending k.
-static constexpr int F32_BM = 64, F32_BN = 64, F32_BK = 32;
+// A workgroup computes a 32-row x 32-output tile (both gate and up for
+// gate/up) with float32 FMAs, in 32-deep K steps.  A step's activation rows
+// (gathered through a_rows, transposed) and weight rows W[k][n0 .. n0+32)
+// (as they lie in memory) sit in one of two LDS buffers; the next step's
+// values are loaded into registers while the current step is multiplied,
+// then written to the other buffer, so a step waits on no global load.
+// Loads put consecutive threads on consecutive addresses; each thread
+// accumulates 2 rows x 2 outputs in registers, in ascending k.
+static constexpr int F32_BM = 32, F32_BN = 32, F32_BK = 32;
 
 template <int MODE>
 __global__ __launch_bounds__(256) void k_f32(KArgs a) {
-  __shared__ float As[F32_BK][F32_BM + 4];
-  __shared__ float Ws0[F32_BK][F32_BN];
-  __shared__ float Ws1[MODE == MODE_GATEUP ? F32_BK : 1][F32_BN];
+  constexpr bool GU = MODE == MODE_GATEUP;
+  constexpr int PA = F32_BM * F32_BK / 256, PW = F32_BK * F32_BN / 256;
+  __shared__ float As[2][F32_BK][F32_BM + 4];
+  __shared__ float Ws0[2][F32_BK][F32_BN];
+  __shared__ float Ws1[2][GU ? F32_BK : 1][F32_BN];
   const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;      // 4 rows x 4 outputs each
+  const int ty = tid >> 4, tx = tid & 15;      // rows 2 ty + i, outputs 2 tx + j
   const int K = a.K, N = a.N;
   const int total = a.tile_count[0] * a.nb_per_tile;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -406,72 +410,95 @@ __global__ __launch_bounds__(256) void k_f32(KArgs a) {
     const bool sh = g == a.P;
     const int n0 = nb * F32_BN;
     const float* W0 = (const float*)(sh ? a.w0_sh : a.w0_arr[g]);
-    const float* W1 = MODE == MODE_GATEUP
-                          ? (const float*)(sh ? a.w1_sh : a.w1_arr[g])
-                          : nullptr;
-    // the activation row each of this thread's staging slots reads
-    const float* arow[F32_BM * F32_BK / 256];
+    const float* W1 = GU ? (const float*)(sh ? a.w1_sh : a.w1_arr[g]) : nullptr;
+    // staging slot i of this thread: activation (row m, k kk) and weight
+    // (k kk, output nn) of a step
+    const float* arow[PA];
 #pragma unroll
-    for (int i = 0; i < F32_BM * F32_BK / 256; ++i) {
+    for (int i = 0; i < PA; ++i) {
       const int m = (tid + 256 * i) / F32_BK;
       const int r = row0 + (m < nrows ? m : 0);
       arow[i] = sh ? (const float*)a.a_shared + (size_t)r * K
                    : (const float*)a.a_routed +
                          (size_t)(a.a_rows ? a.a_rows[r] : r) * K;
     }
-    float acc0[4][4], acc1[4][4];
+    float ra[PA], rw0[PW], rw1[PW];
+    auto fetch = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc0[i][j] = acc1[i][j] = 0.0f;
-    for (int k0 = 0; k0 < K; k0 += F32_BK) {
-      __syncthreads();                         // previous step's readers
-#pragma unroll
-      for (int i = 0; i < F32_BM * F32_BK / 256; ++i) {
+      for (int i = 0; i < PA; ++i) {
         const int idx = tid + 256 * i;
         const int m = idx / F32_BK, kk = idx % F32_BK;
-        As[kk][m] = (m < nrows && k0 + kk < K) ? arow[i][k0 + kk] : 0.0f;
+        ra[i] = (m < nrows && k0 + kk < K) ? arow[i][k0 + kk] : 0.0f;
       }
 #pragma unroll
-      for (int i = 0; i < F32_BK * F32_BN / 256; ++i) {
+      for (int i = 0; i < PW; ++i) {
         const int idx = tid + 256 * i;
         const int kk = idx / F32_BN, nn = idx % F32_BN;
         const bool in = k0 + kk < K && n0 + nn < N;
         const size_t o = (size_t)(k0 + kk) * N + n0 + nn;
-        Ws0[kk][nn] = in ? W0[o] : 0.0f;
-        if (MODE == MODE_GATEUP) Ws1[kk][nn] = in ? W1[o] : 0.0f;
+        rw0[i] = in ? W0[o] : 0.0f;
+        if (GU) rw1[i] = in ? W1[o] : 0.0f;
       }
-      __syncthreads();
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < PA; ++i) {
+        const int idx = tid + 256 * i;
+        As[buf][idx % F32_BK][idx / F32_BK] = ra[i];
+      }
+#pragma unroll
+      for (int i = 0; i < PW; ++i) {
+        const int idx = tid + 256 * i;
+        Ws0[buf][idx / F32_BN][idx % F32_BN] = rw0[i];
+        if (GU) Ws1[buf][idx / F32_BN][idx % F32_BN] = rw1[i];
+      }
+    };
+    float acc0[2][2], acc1[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc0[i][j] = acc1[i][j] = 0.0f;
+    fetch(0);
+    __syncthreads();                           // the last item's readers
+    stash(0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = 0; k0 < K; k0 += F32_BK) {
+      const bool more = k0 + F32_BK < K;
+      if (more) fetch(k0 + F32_BK);            // in flight during the step
 #pragma unroll 8
       for (int kk = 0; kk < F32_BK; ++kk) {
-        float av[4], b0[4], b1[4];
+        float av[2], b0[2], b1[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+        for (int i = 0; i < 2; ++i) av[i] = As[buf][kk][ty * 2 + i];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          b0[j] = Ws0[kk][tx * 4 + j];
-          if (MODE == MODE_GATEUP) b1[j] = Ws1[kk][tx * 4 + j];
+        for (int j = 0; j < 2; ++j) {
+          b0[j] = Ws0[buf][kk][tx * 2 + j];
+          if (GU) b1[j] = Ws1[buf][kk][tx * 2 + j];
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < 2; ++j) {
             acc0[i][j] = __builtin_fmaf(av[i], b0[j], acc0[i][j]);
-            if (MODE == MODE_GATEUP)
-              acc1[i][j] = __builtin_fmaf(av[i], b1[j], acc1[i][j]);
+            if (GU) acc1[i][j] = __builtin_fmaf(av[i], b1[j], acc1[i][j]);
           }
       }
+      // the other buffer was last read before the previous barrier
+      if (more) stash(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = ty * 4 + i;
+    for (int i = 0; i < 2; ++i) {
+      const int r = ty * 2 + i;
       if (r >= nrows) continue;
       const int row = row0 + r;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + tx * 4 + j;
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + tx * 2 + j;
         if (n >= N) continue;
-        if (MODE == MODE_GATEUP) {
+        if (GU) {
           const size_t hr = (size_t)(sh ? a.cap : 0) + row;
           ((float*)a.h_out)[hr * N + n] = silu_f32(acc0[i][j]) * acc1[i][j];
         } else {
