@@ -70,23 +70,23 @@ COUNTERS = {
     "tiny": {
         "kernel": "k_f32<0>", "profile": "profiles/layer_f32_tiny.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "35f656de498adb24",
-        "fetch_kib": 1333.0, "fetch_factor": 1.5785,
+        "sha": "8dc1f4b35590953a",
+        "fetch_kib": 1831.6, "fetch_factor": 1.5784,
         "write_kib": 128.0, "write_factor": 1.0},
     "decode": {
         "kernel": "k_stream_bf16<0, 2>", "profile": "profiles/layer_stream_bf16_decode.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "35f656de498adb24",
-        "fetch_kib": 794480.7, "fetch_factor": 1.9976,
-        "write_kib": 988.9, "write_factor": 1.0,
-        "mfma_util": 0.051},
+        "sha": "8dc1f4b35590953a",
+        "fetch_kib": 794476.7, "fetch_factor": 1.9976,
+        "write_kib": 988.7, "write_factor": 1.0,
+        "mfma_util": 0.052},
     "decode_skewed": {
         "kernel": "k_stream_bf16<0, 2>", "profile": "profiles/layer_stream_bf16_decode_skewed.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "35f656de498adb24",
-        "fetch_kib": 207547.2, "fetch_factor": 1.9976,
-        "write_kib": 876.2, "write_factor": 1.0,
-        "mfma_util": 0.051},
+        "sha": "8dc1f4b35590953a",
+        "fetch_kib": 207722.8, "fetch_factor": 1.9976,
+        "write_kib": 875.4, "write_factor": 1.0,
+        "mfma_util": 0.052},
     "prefill": {
         "kernel": "k_gemm_bf16<0, 4, 2, 2, 4>", "profile": "profiles/layer_gemm_bf16_prefill.md",
         "files": ["expert_moe_fp32_amd/csrc/gemm_bf16.hip", "expert_moe_fp32_amd/csrc/common.h"],
