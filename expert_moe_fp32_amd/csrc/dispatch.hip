@@ -56,14 +56,17 @@ __device__ __forceinline__ void load_local_ids(const int32_t* ids, int t,
   }
 }
 
-// For every local expert e < L, in ascending e, calls sink(e, m) on all lanes
-// with m = the ballot of the lanes whose token picked e (a token picks an
-// expert at most once).  With L <= 256 each lane first folds its picks into
-// a 256-bit mask, so an expert costs one shift-and-ballot; beyond that every
-// expert is compared against every slot.
-template <class Sink>
+// For every local expert e < L calls store(e, m), with m = the ballot of the
+// lanes whose token picked e (a token picks an expert at most once), on one
+// lane.  With L <= 256 each lane first folds its picks into a 256-bit mask,
+// so an expert costs one shift-and-ballot; the ballots are gathered into
+// the registers of lane e % 64 (a select, no branch per expert) and stored
+// from there, every lane at most four times.  Beyond 256 every expert is
+// compared against every slot and stored from lane 0.
+template <class Store>
 __device__ __forceinline__ void for_each_expert_ballot(
-    const int (&le)[MOE_KMAX], int L, Sink sink) {
+    const int (&le)[MOE_KMAX], int L, Store store) {
+  const int lane = threadIdx.x & 63;
   if (L <= 256) {
     uint64_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
 #pragma unroll
@@ -76,20 +79,28 @@ __device__ __forceinline__ void for_each_expert_ballot(
       m2 |= w == 2 ? bit : 0ull;
       m3 |= w == 3 ? bit : 0ull;
     }
-    auto word = [&](uint64_t mw, int base) {
+    uint64_t mine[4] = {0ull, 0ull, 0ull, 0ull};
+    auto word = [&](uint64_t mw, int base, uint64_t& dst) {
       const int n = min(64, L - base);
-      for (int b = 0; b < n; ++b) sink(base + b, __ballot((mw >> b) & 1ull));
+      for (int b = 0; b < n; ++b) {
+        const uint64_t m = __ballot((mw >> b) & 1ull);
+        dst = lane == b ? m : dst;
+      }
     };
-    word(m0, 0);
-    if (L > 64) word(m1, 64);
-    if (L > 128) word(m2, 128);
-    if (L > 192) word(m3, 192);
+    word(m0, 0, mine[0]);
+    if (L > 64) word(m1, 64, mine[1]);
+    if (L > 128) word(m2, 128, mine[2]);
+    if (L > 192) word(m3, 192, mine[3]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (64 * w + lane < L) store(64 * w + lane, mine[w]);
   } else {
     for (int e = 0; e < L; ++e) {
       bool has = false;
 #pragma unroll
       for (int j = 0; j < MOE_KMAX; ++j) has |= le[j] == e;
-      sink(e, __ballot(has));
+      const uint64_t m = __ballot(has);
+      if (lane == 0) store(e, m);
     }
   }
 }
@@ -117,7 +128,7 @@ __global__ __launch_bounds__(256) void k_local_hist(
   int le[MOE_KMAX];
   load_local_ids(ids, t, T, k, e0, L, le);
   for_each_expert_ballot(le, L, [&](int e, uint64_t m) {
-    if (lane == 0) wave_cnt[wv * L + e] = __popcll(m);
+    wave_cnt[wv * L + e] = __popcll(m);
   });
   __syncthreads();
   for (int e = threadIdx.x; e < L; e += blockDim.x)
@@ -245,10 +256,8 @@ __global__ __launch_bounds__(256) void k_permute(
   int le[MOE_KMAX];
   load_local_ids(ids, t, T, k, e0, L, le);
   for_each_expert_ballot(le, L, [&](int e, uint64_t m) {
-    if (lane == 0) {
-      bal[wv * L + e] = m;
-      wave_cnt[wv * L + e] = __popcll(m);
-    }
+    bal[wv * L + e] = m;
+    wave_cnt[wv * L + e] = __popcll(m);
   });
   __syncthreads();
   if (t >= T) return;
@@ -266,12 +275,13 @@ __global__ __launch_bounds__(256) void k_permute(
             __popcll(bal[wv * L + e] & lt);  // earlier lanes of this wave
     for (int v = 0; v < wv; ++v) n += wave_cnt[v * L + e];
     const int R = rep ? min(max(rep[e], 1), max_rep) : 1;
-    const int p = l2p ? l2p[e * max_rep + (n % R)] : e;
+    const int nq = R == 1 ? n : n / R;       // one replica: no division
+    const int p = l2p ? l2p[e * max_rep + (n - nq * R)] : e;
     if (p < 0 || p >= P) {                   // a map entry out of range:
       pair_row[o] = -1;                      // the pair is dropped
       continue;
     }
-    const int row = offsets[p] + n / R;
+    const int row = offsets[p] + nq;
     pair_row[o] = row;
     row_token[row] = t;
     row_weight[row] = w[o];
@@ -306,6 +316,19 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
   // ids, rather than read from global memory where they are needed: two
   // dependent round trips fewer on this single-workgroup path.
   const bool map_lds = a.l2p && L * a.max_rep <= kSmallMap;
+  // the token's ids and route weights are requested first: their latency
+  // overlaps the LDS set-up below
+  int gid[MOE_KMAX];
+  float wj[MOE_KMAX];
+#pragma unroll
+  for (int j = 0; j < MOE_KMAX; ++j) {
+    gid[j] = -1;
+    wj[j] = 0.0f;
+    if (j < k && t < T) {
+      gid[j] = a.ids[(size_t)t * k + j];
+      wj[j] = a.w[(size_t)t * k + j];
+    }
+  }
   for (int i = t; i < L; i += 1024)
     reps[i] = a.rep ? min(max(a.rep[i], 1), a.max_rep) : 1;
   if (map_lds)
@@ -314,26 +337,20 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
   for (int i = t; i <= P; i += 1024) pc[i] = 0;
   __syncthreads();
   int le[MOE_KMAX];
-  float wj[MOE_KMAX];                      // route weights, loaded with the ids
 #pragma unroll
   for (int j = 0; j < MOE_KMAX; ++j) {
     le[j] = -1;
-    wj[j] = 0.0f;
     if (j < k && t < T) {
-      const int gid = a.ids[(size_t)t * k + j];
-      wj[j] = a.w[(size_t)t * k + j];
       // expert counts only when asked for, and only of ids in [0, E)
-      if (x.counts && (unsigned)gid < (unsigned)x.E) atomicAdd(&cnt[gid], 1);
-      const int e = gid - a.expert_begin;
+      if (x.counts && (unsigned)gid[j] < (unsigned)x.E) atomicAdd(&cnt[gid[j]], 1);
+      const int e = gid[j] - a.expert_begin;
       if (e >= 0 && e < L) le[j] = e;
     }
   }
   const uint64_t lt = lanemask_lt();
   for_each_expert_ballot(le, L, [&](int e, uint64_t m) {
-    if (lane == 0) {
-      bal[wv * kSmallL + e] = m;
-      wpre[wv * kSmallL + e] = __popcll(m);
-    }
+    bal[wv * kSmallL + e] = m;
+    wpre[wv * kSmallL + e] = __popcll(m);
   });
   __syncthreads();
   if (x.counts)
@@ -383,13 +400,14 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
     }
     const int n = wpre[wv * kSmallL + e] + __popcll(bal[wv * kSmallL + e] & lt);
     const int R = reps[e];
-    const int mi = e * a.max_rep + (n % R);
+    const int nq = R == 1 ? n : n / R;       // one replica: no division
+    const int mi = e * a.max_rep + (n - nq * R);
     const int p = !a.l2p ? e : map_lds ? maps[mi] : a.l2p[mi];
     if (p < 0 || p >= P) {
       a.pair_row[o] = -1;
       continue;
     }
-    const int row = pc[p] + n / R;
+    const int row = pc[p] + nq;
     a.pair_row[o] = row;
     a.row_token[row] = t;
     a.row_weight[row] = wj[j];
