@@ -82,6 +82,17 @@ def check_against_oracle(wl, got, l2p=None, rep=None, P=None):
     # the largest share: 1024 local experts, k = 16
     ("tiny", dict(T=500, E=1024, num_local=1024, expert_begin=0, k=16, H=64,
                   I=64)),
+    # just past the single-workgroup kernel's 1024 tokens (a last block of
+    # one token), 64 local experts over 20 blocks, a last block of one token
+    # at 8193, and 65 local experts (the ballot words past the first)
+    ("tiny", dict(T=1025, E=64, num_local=16, expert_begin=8, k=4, H=64,
+                  I=64)),
+    ("tiny", dict(T=5000, E=128, num_local=64, expert_begin=64, k=8, H=64,
+                  I=64)),
+    ("tiny", dict(T=8193, E=64, num_local=32, expert_begin=0, k=6, H=64,
+                  I=64)),
+    ("tiny", dict(T=3000, E=256, num_local=65, expert_begin=0, k=8, H=64,
+                  I=64)),
 ])
 def test_dispatch_matches_oracle(name, kw):
     wl = make_workload(name, seed=0, **kw)
@@ -118,6 +129,16 @@ def test_dispatch_edge_cases():
     assert d.phys_counts.tolist() == [0, 300, 0, 0]
     one = make_workload("tiny", seed=1, T=1)
     check_against_oracle(one, run_dispatch(one))
+    # the same skew over 3000 tokens (the multi-block kernels)
+    big = make_workload("tiny", seed=0, T=3000, E=16, num_local=4,
+                        expert_begin=12, k=2, H=64, I=64)
+    logits = np.full((3000, 16), -5.0, dtype=np.float32)
+    logits[:, 13] = 3.0
+    logits[:, 2] = 2.0
+    logits[::2, 2] = 4.0
+    big._cache["logits"] = logits
+    d = check_against_oracle(big, run_dispatch(big))
+    assert d.phys_counts.tolist() == [0, 3000, 0, 0]
 
 
 def test_fp8_quantiser_every_bf16_value():
