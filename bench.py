@@ -12,7 +12,8 @@ hot local expert), prefill, skewed (prefill shape with a Zipf logit bias,
 identity placement), skewed_eplb (the same batch with the 8 hottest local
 experts given a second physical copy, placed from the first pass's expert
 counts by the library's moe_eplb_hottest_map; the layer then reads 40
-physical experts' weights), fp8, lowlat (128-token FP8 decode batch).
+physical experts' weights), fp8, lowlat (128-token FP8 decode batch),
+lowlat_skewed (lowlat with a Zipf logit bias).
 
 With the default workload the same run also times the prefill workload (the
 metric's other half, TFLOP/s against the MFMA peak) and reports it in a
@@ -52,7 +53,7 @@ METRIC = "MoE-layer tokens/s on 1 MI355X; decode HBM TB/s and prefill TFLOP/s vs
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 WORKLOADS = ["tiny", "decode", "decode_skewed", "prefill", "skewed",
-             "skewed_eplb", "fp8", "lowlat"]
+             "skewed_eplb", "fp8", "lowlat", "lowlat_skewed"]
 
 
 # Counter figures per launch of each workload's dominant (gate/up) kernel,
@@ -531,7 +532,7 @@ def main():
         n = args.cpu_tokens or {"tiny": 128, "decode": 256,
                                 "decode_skewed": 256, "prefill": 16,
                                 "skewed": 16, "fp8": 16,
-                                "lowlat": 8}[wl.name]
+                                "lowlat": 8, "lowlat_skewed": 8}[wl.name]
         rng = np.random.default_rng(1)
         tok = np.sort(rng.choice(wl.T, size=min(n, wl.T), replace=False))
         log(f"bench: CPU oracle on {len(tok)} tokens ...")

@@ -25,6 +25,8 @@ always-on shared expert, one EP rank's contiguous share of experts):
   top-8, FP8 dispatch (activations in E4M3 per token per 128 channels) and
   BF16 combine; the expert is DeepSeek-V3's (I=2048, 256 experts, 32 local),
   weights as in ``fp8``.
+* ``lowlat_skewed`` ``lowlat`` plus the Zipf s=1.2 logit bias of ``skewed``:
+  an FP8 decode batch in which one local expert holds most of the local rows.
 
 Stored layouts (row-major):
 * ``logits`` [T, E] float32, ``bias`` [E] float32 or None;
@@ -70,6 +72,10 @@ CONFIGS: Dict[str, dict] = {
                           expert_begin=0, num_local=32, shared=False,
                           act="bf16", wdt="bf16", out="bf16", bias="zipf",
                           zipf_s=1.2),
+    "lowlat_skewed": dict(wid=8, T=128, H=7168, I=2048, E=256, k=8,
+                          expert_begin=0, num_local=32, shared=False,
+                          act="bf16", wdt="fp8", out="bf16", bias="zipf",
+                          zipf_s=1.2, quant_block=128),
 }
 
 _TENSOR_LOGITS, _TENSOR_X, _TENSOR_W, _TENSOR_SHARED, _TENSOR_PERM = 1, 2, 3, 4, 5

@@ -108,6 +108,23 @@ def test_fp8_layer_reduced(kw):
     complete_check(make_workload("fp8", seed=31, **kw))
 
 
+@pytest.mark.parametrize("T,E,shared", [(128, 32, False), (300, 64, False),
+                                        (45, 32, False), (100, 32, True)])
+def test_fp8_streaming_group_of_many_tiles(T, E, shared):
+    """The register weight-streaming recipe (a few rows per expert) with a
+    group of more than one 32-row tile: local expert 3 on every token (128,
+    300 or 45 rows in balanced tiles of up to 32), or the shared expert's T
+    rows."""
+    wl = make_workload("fp8", seed=33, T=T, H=512, I=512, E=E, num_local=8,
+                       k=4, shared=shared)
+    if not shared:
+        logits = wl.logits.copy()
+        logits[:, 3] += 20.0
+        wl._cache["logits"] = logits
+    st = complete_check(wl)
+    assert st["codes"] > 0
+
+
 def test_fp8_weights_in_either_storage_order_give_the_same_layer():
     """Weights handed over in the logical layout (W_gate, W_up [H][I],
     W_down [I][H]) or transposed give bit-identical outputs."""
