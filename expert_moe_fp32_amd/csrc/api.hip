@@ -97,7 +97,9 @@ FfnScratch carve_ffn(Carver& c, const moe_problem* p) {
   // rows of their group
   f.max_tiles = (int)(p->num_physical + 2 + (hrows + 15) / 16 + (hrows + 7) / 8);
   f.tiles = c.take<int4>((size_t)f.max_tiles);
-  // 128-row tiles: at most one partial tile per group
+  // 128-row tiles (or the FP8 streaming down pass's tiles: one per group of
+  // up to 32 rows, tall tiles of up to 128 beyond): at most one partial tile
+  // per group
   f.tiles_down = c.take<int4>((size_t)p->num_physical + 2 + hrows / 128);
   f.tile_count = c.take<int32_t>(4);
   return f;
@@ -484,6 +486,11 @@ static moe_status layer_impl(const moe_problem* p, const float* logits,
   extras.BM = ffn_tile_rows(p->act_dtype, p->weight_dtype, rows_hint(p),
                             p->H, p->I, &extras.balanced);
   extras.tallBM = ffn_tall_rows(p->act_dtype, p->weight_dtype, extras.BM);
+  extras.tallBM2 = ffn_down_tall_rows(p->weight_dtype, extras.BM);
+  if (extras.tallBM2) {           // the down pass's own list
+    extras.tiles2 = L.f.tiles_down;
+    extras.count2 = L.f.tile_count + 1;
+  }
   extras.has_shared = p->has_shared;
   // FP8 recipe: the router and the activation quantiser share one launch
   // (the quantiser reads only x), so the router's latency hides under the

@@ -69,17 +69,20 @@ __device__ __forceinline__ int tile_split(int rows, int BM, int balanced,
 }
 
 // Tiles of one group under a per-group choice: a group of more than BM rows
-// is cut into (balanced) tall tiles of up to tallBM rows, each listed four
-// times as quarters (the streaming kernel then reads each weight byte once
-// per tall tile instead of once per BM rows); otherwise tile_split(rows, BM,
-// balanced).  tallBM = 0 keeps one tile height for every group.  Returns
-// the number of descriptors; *tall says whether they are quarters (the
-// fourth descriptor field then holds 1 + quarter).
+// is cut into (balanced) tall tiles of up to |tallBM| rows instead of
+// tile_split(rows, BM, balanced), so a streaming kernel reads each weight
+// byte once per tall tile rather than once per BM rows.  tallBM > 0: each
+// tall tile is listed four times, as quarters (the fourth descriptor field
+// holds 1 + quarter; the bf16 streaming kernel); tallBM < 0: each is listed
+// once with the fourth field 1 (the FP8 streaming kernel's down pass);
+// tallBM = 0 keeps one tile height for every group.  Returns the number of
+// descriptors; *tall is 0 (ordinary), 1 (quarters) or 2 (listed once).
 __device__ __forceinline__ int group_tiles(int rows, int BM, int balanced,
                                            int tallBM, int* per, int* tall) {
-  if (tallBM > 0 && rows > BM) {
-    *tall = 1;
-    return 4 * tile_split(rows, tallBM, 1, per);
+  if (tallBM != 0 && rows > BM) {
+    *tall = tallBM > 0 ? 1 : 2;
+    const int n = tile_split(rows, tallBM > 0 ? tallBM : -tallBM, 1, per);
+    return tallBM > 0 ? 4 * n : n;
   }
   *tall = 0;
   return tile_split(rows, BM, balanced, per);
@@ -91,10 +94,10 @@ __device__ __forceinline__ void write_group_tiles(int4* tiles, int i, int g,
                                                   int tall) {
   for (int r = 0; r < rows; r += per) {
     const int n = min(per, rows - r);
-    if (tall) {
+    if (tall == 1) {
       for (int qd = 0; qd < 4; ++qd) tiles[i++] = make_int4(g, start + r, n, 1 + qd);
     } else {
-      tiles[i++] = make_int4(g, start + r, n, 0);
+      tiles[i++] = make_int4(g, start + r, n, tall ? 1 : 0);
     }
   }
 }
@@ -169,7 +172,11 @@ struct DispatchExtras {
   int32_t* tile_count;
   int BM, has_shared;
   int balanced;           // near-equal tiles (multiples of 16 rows)
-  int tallBM;             // > 0: groups of more than BM rows in tall tiles
+  int tallBM;             // != 0: groups of more than BM rows in tall
+                          // tiles (see group_tiles)
+  int4* tiles2;           // or null: a second list of the same BM and
+  int32_t* count2;        //   balance with tallBM2 (the FP8 streaming
+  int tallBM2;            //   recipe's down pass), count in count2[0]
 };
 bool dispatch_small_ok(int T, int E, int L, int P);
 // FP8 layer: router top-k (E <= 256) and the activation quantiser in one
@@ -232,7 +239,9 @@ struct FfnArgs {
   float* y_routed;                    // [cap][H]
   float* y_shared;                    // [T][H]
   int4* tiles;                        // tile list scratch
-  int4* tiles_down;                   // second list (128-row tiles for down)
+  int4* tiles_down;                   // second list: 128-row tiles for the
+                                      // bf16 down pass when H % 256 != 0, or
+                                      // the FP8 streaming down pass's tiles
   int32_t* tile_count;                // [2] scratch: counts of the lists
   int max_tiles;
   bool tiles_ready;                   // tile list already written
@@ -245,14 +254,19 @@ hipError_t launch_ffn_fp8(FfnArgs& a, hipStream_t s);
 int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int I, int* balanced);
 // rows of the tall tiles that groups larger than a tile get (0: none)
 int ffn_tall_rows(int act, int wdt, int BM);
+// tall rows of the down pass's own tile list (0: down uses the first list)
+int ffn_down_tall_rows(int wdt, int BM);
 int ffn_fp8_tile_rows(int rows_hint, int H, int I, int* balanced);
 // gate/up LDS-ring GEMM over a list of tiles of up to gemm_tile_rows() rows
 hipError_t launch_gemm_bf16_gateup(const FfnArgs& f, hipStream_t s);
 hipError_t launch_gemm_bf16_down(const FfnArgs& f, hipStream_t s);
 int gemm_tile_rows();
+// tile list of BM-row tiles (see group_tiles), and when tiles2 is non-null
+// a second list of the same tiles but tallBM2
 hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
                               int T, int BM, int balanced, int tallBM,
-                              int4* tiles, int32_t* count, hipStream_t s);
+                              int4* tiles, int32_t* count, int tallBM2,
+                              int4* tiles2, int32_t* count2, hipStream_t s);
 
 // a K x N matrix stored KN or NK -> its prepared form for `dtype` (float32
 // [K][N]; bf16 16x32 or fp8 16x128 packed operand blocks)

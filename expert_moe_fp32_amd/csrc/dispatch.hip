@@ -139,32 +139,42 @@ __global__ __launch_bounds__(256) void k_local_hist(
       block_ecounts[(size_t)blockIdx.x * E + e] = ehist[e];
 }
 
-// FFN tile list from the segment offsets held in LDS (off[0 .. P]) by a
-// single workgroup: wavefront 0 counts each group's tiles and scans them
-// into tb (G + 1 entries, G = P + shared), the workgroup barrier follows,
-// then every thread writes its groups' tiles.  Called by all threads.
+// FFN tile lists (tiles of BM rows, see group_tiles) from the segment
+// offsets held in LDS (off[0 .. P]) by a single workgroup: x.tiles, and
+// x.tiles2 (the same tiles with x.tallBM2) when set.  Wavefront 0 counts
+// each group's tiles and scans them into tb (and tb2; G + 1 entries each,
+// G = P + shared), the workgroup barrier follows, then every thread writes
+// its groups' tiles.  Called by all threads.
 __device__ void tile_list_from_offsets(const int32_t* off, int P, int T,
-                                       const DispatchExtras& x, int32_t* tb) {
+                                       const DispatchExtras& x, int32_t* tb,
+                                       int32_t* tb2) {
   const int G = P + (x.has_shared ? 1 : 0);
+  const bool two = x.tiles2 != nullptr;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int nt_carry = 0;
+    int carry = 0, carry2 = 0;
     for (int base = 0; base < G; base += 64) {
       const int g = base + lane;
-      int nt = 0;
+      int nt = 0, nt2 = 0;
       if (g < G) {
         const int rows = g < P ? off[g + 1] - off[g] : T;
         int per, tall;
         nt = group_tiles(rows, x.BM, x.balanced, x.tallBM, &per, &tall);
+        if (two) nt2 = group_tiles(rows, x.BM, x.balanced, x.tallBM2, &per, &tall);
       }
-      int tot;
+      int tot, tot2 = 0;
       const int ex = wave_excl_scan(nt, &tot);
-      if (g < G) tb[g] = nt_carry + ex;
-      nt_carry += tot;
+      const int ex2 = two ? wave_excl_scan(nt2, &tot2) : 0;
+      if (g < G) {
+        tb[g] = carry + ex;
+        if (two) tb2[g] = carry2 + ex2;
+      }
+      carry += tot;
+      carry2 += tot2;
     }
     if (lane == 0) {
-      tb[G] = nt_carry;
-      x.tile_count[0] = nt_carry;
+      x.tile_count[0] = carry;
+      if (two) x.count2[0] = carry2;
     }
   }
   __syncthreads();
@@ -175,6 +185,10 @@ __device__ void tile_list_from_offsets(const int32_t* off, int P, int T,
     int per, tall;
     group_tiles(rows, x.BM, x.balanced, x.tallBM, &per, &tall);
     write_group_tiles(x.tiles, tb[g], g, start, rows, per, tall);
+    if (two) {
+      group_tiles(rows, x.BM, x.balanced, x.tallBM2, &per, &tall);
+      write_group_tiles(x.tiles2, tb2[g], g, start, rows, per, tall);
+    }
   }
 }
 
@@ -185,7 +199,7 @@ __global__ __launch_bounds__(1024) void k_scan(
     int32_t* __restrict__ offsets, int T, DispatchExtras x,
     const int32_t* __restrict__ block_ecounts) {
   __shared__ int32_t pc[MOE_LMAX + 1];
-  __shared__ int32_t tb[MOE_LMAX + 2];
+  __shared__ int32_t tb[MOE_LMAX + 2], tb2[MOE_LMAX + 2];
   if (x.counts) {                          // expert counts: sum the block rows
     for (int e = threadIdx.x; e < x.E; e += blockDim.x) {
       int c = 0;
@@ -238,7 +252,7 @@ __global__ __launch_bounds__(1024) void k_scan(
   }
   if (x.tiles) {                           // uniform
     __syncthreads();
-    tile_list_from_offsets(pc, P, T, x, tb);
+    tile_list_from_offsets(pc, P, T, x, tb, tb2);
   }
 }
 
@@ -305,7 +319,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
                                                          DispatchExtras x) {
   __shared__ int32_t cnt[MOE_EMAX];
   __shared__ int32_t pc[MOE_LMAX + 1];
-  __shared__ int32_t tb[MOE_LMAX + 2];
+  __shared__ int32_t tb[MOE_LMAX + 2], tb2[MOE_LMAX + 2];
   __shared__ int32_t wpre[16 * kSmallL];
   __shared__ uint64_t bal[16 * kSmallL];    // per wavefront: ballot per expert
   __shared__ int32_t reps[kSmallL];         // replica counts (clamped)
@@ -387,7 +401,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(DispatchArgs a,
     }
   }
   __syncthreads();
-  if (x.tiles) tile_list_from_offsets(pc, P, T, x, tb);   // uniform
+  if (x.tiles) tile_list_from_offsets(pc, P, T, x, tb, tb2);   // uniform
   if (t >= T) return;
 #pragma unroll
   for (int j = 0; j < MOE_KMAX; ++j) {

@@ -67,20 +67,21 @@ struct KArgs {
 // row offsets[g]; group P (shared) has T rows starting at 0.  Output:
 // tiles[i] = {group, first row, rows, 0}, count[0] = number of tiles.
 // Writes the tile list for tiles of BM rows (balanced: tile_split's
-// near-equal tiles) and, when tiles2 is non-null, a second plain list for
-// tiles of BM2 rows, each with its count.
+// near-equal tiles; tallBM: see group_tiles) and, when tiles2 is non-null,
+// a second list for tiles of BM2 rows (balanced2, tallBM2), each with its
+// count.
 __global__ __launch_bounds__(1024) void k_build_tiles(
     const int32_t* __restrict__ offsets, int P, int has_shared, int T, int BM,
     int balanced, int tallBM, int4* __restrict__ tiles,
-    int32_t* __restrict__ count, int BM2, int4* __restrict__ tiles2,
-    int32_t* __restrict__ count2) {
+    int32_t* __restrict__ count, int BM2, int balanced2, int tallBM2,
+    int4* __restrict__ tiles2, int32_t* __restrict__ count2) {
   __shared__ int32_t base[2][MOE_LMAX + 2];
   const int G = P + (has_shared ? 1 : 0);
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
     const int rows = g < P ? offsets[g + 1] - offsets[g] : T;
     int per, tall;
     base[0][g + 1] = group_tiles(rows, BM, balanced, tallBM, &per, &tall);
-    base[1][g + 1] = (rows + BM2 - 1) / BM2;
+    base[1][g + 1] = group_tiles(rows, BM2, balanced2, tallBM2, &per, &tall);
   }
   __syncthreads();
   if (threadIdx.x < 2) {
@@ -98,9 +99,8 @@ __global__ __launch_bounds__(1024) void k_build_tiles(
     group_tiles(rows, BM, balanced, tallBM, &per, &tall);
     write_group_tiles(tiles, base[0][g], g, start, rows, per, tall);
     if (tiles2) {
-      int i = base[1][g];
-      for (int r = 0; r < rows; r += BM2, ++i)
-        tiles2[i] = make_int4(g, start + r, min(BM2, rows - r), 0);
+      group_tiles(rows, BM2, balanced2, tallBM2, &per, &tall);
+      write_group_tiles(tiles2, base[1][g], g, start, rows, per, tall);
     }
   }
 }
@@ -528,9 +528,11 @@ int ffn_tile_rows(int act, int wdt, int rows_hint, int H, int I, int* balanced) 
 
 hipError_t launch_build_tiles(const int32_t* offsets, int P, int has_shared,
                               int T, int BM, int balanced, int tallBM,
-                              int4* tiles, int32_t* count, hipStream_t s) {
+                              int4* tiles, int32_t* count, int tallBM2,
+                              int4* tiles2, int32_t* count2, hipStream_t s) {
   k_build_tiles<<<1, 1024, 0, s>>>(offsets, P, has_shared, T, BM, balanced,
-                                   tallBM, tiles, count, BM, nullptr, nullptr);
+                                   tallBM, tiles, count, BM, balanced, tallBM2,
+                                   tiles2, count2);
   return hipGetLastError();
 }
 
@@ -560,12 +562,13 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
   if (!f.tiles_ready)
     k_build_tiles<<<1, 1024, 0, s>>>(f.offsets, f.P, f.has_shared, f.T, BM,
                                      balanced, tallBM, f.tiles, f.tile_count,
-                                     TBM, down_list ? f.tiles_down : nullptr,
+                                     TBM, 0, 0,
+                                     down_list ? f.tiles_down : nullptr,
                                      f.tile_count + 1);
   else if (down_list)
     k_build_tiles<<<1, 1024, 0, s>>>(f.offsets, f.P, f.has_shared, f.T, TBM, 0,
-                                     0, f.tiles_down, f.tile_count + 1, TBM,
-                                     nullptr, nullptr);
+                                     0, f.tiles_down, f.tile_count + 1, TBM, 0,
+                                     0, nullptr, nullptr);
   if (f.events) hipEventRecord(f.events[0], s);
   // bound on the tile count for the grid size
   const long hrows = (long)f.cap + (f.has_shared ? f.T : 0);

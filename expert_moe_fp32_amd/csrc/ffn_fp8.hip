@@ -564,7 +564,9 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
 }
 
 // ------------------------------------------------- weight-streaming kernel
-// For groups of a few rows (decode-sized tiles of up to 16 * NMB = 32 rows).  A workgroup of 8
+// For groups of a few rows (decode-sized tiles of up to 16 * NMB = 32 rows;
+// in the down pass a larger group's tall tiles of up to 128 rows run with
+// NMB = 8).  A workgroup of 8
 // wavefronts owns one tile and a group of output channels; each wavefront
 // owns two 16-channel weight columns -- gate and up of the same channels
 // (128 channels an item), or two down columns 128 channels apart (256 an
@@ -584,35 +586,25 @@ __global__ __launch_bounds__(512) void k_ring_fp8(K8Args a) {
 // block has landed" is one fixed vmcnt.  The weight scales of the two
 // columns sit one per lane (K <= 16384) and are read with readlane, so the
 // loop issues no other load.
+//
+// One item (tile, nb) of k_wstream_fp8 with NMB row blocks; the LDS ring
+// (4 stages of activation blocks la* and row scales ls*) is sized for the
+// largest NMB the kernel runs.
 template <int MODE, int NMB>
-__global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
+__device__ __forceinline__ void wstream_item(const K8Args& a, int4 td, int nb,
+                                             u32x4_t* la0, u32x4_t* la1,
+                                             u32x4_t* la2, u32x4_t* la3,
+                                             float* ls0, float* ls1,
+                                             float* ls2, float* ls3) {
   constexpr int NAB = 2 * NMB;                   // 8-row activation blocks
   constexpr int A_PER = (NAB + 7) / 8;
   constexpr int NRS = (16 * NMB + 63) / 64;      // 64-row scale slices
   constexpr int C = A_PER + 1 + 4;               // loads per block per wave
-  __shared__ u32x4_t la0[NMB * 128], la1[NMB * 128], la2[NMB * 128], la3[NMB * 128];
-  __shared__ __attribute__((aligned(16))) float ls0[(NRS + 1) * 64],
-      ls1[(NRS + 1) * 64], ls2[(NRS + 1) * 64], ls3[(NRS + 1) * 64];  // slice NRS: dump
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, q = lane >> 4;
   const int K = a.K, KB = K / 128;
-  const int total = a.tile_count[0] * a.nb_per_tile;
-  // As many workgroups as make the rounds of the persistent loop equal (a
-  // multiple of 8 for the XCD mapping); the rest exit at once.  A short last
-  // round leaves the weight stream to a fraction of the CUs (low-latency
-  // layer -2 %).
-  const int rounds = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int G = min((int)gridDim.x, (((total + rounds - 1) / max(rounds, 1)) + 7) & ~7);
-  const int per_xcd = G >> 3;
-  if ((int)blockIdx.x >= G) return;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  for (int base = 0; base < total; base += G) {
-    const int item = base + xcd * per_xcd + slot;
-    if (item >= total) continue;                 // uniform for the workgroup
-    const int tile = item / a.nb_per_tile;
-    const int nb = item - tile * a.nb_per_tile;
-    const int4 td = a.tiles[tile];
+  {
     const int g = td.x, row0 = td.y, nrows = td.z;
     const bool sh = g == a.P;
     const int nmb = (nrows + 15) >> 4;
@@ -789,7 +781,7 @@ __global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
         }
       lds_barrier();
       hq_store(hq, a, sh, row0, nrows, nb, 512);
-      continue;
+      return;
     }
     // Epilogue from a wave-uniform 64-bit base and 32-bit offsets; N goes
     // through an opaque move so the offsets are formed here rather than
@@ -809,6 +801,45 @@ __global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
         out[off + (cb1 - cb0) * 16] = acc[m][1][r];
       }
     }
+  }
+}
+
+// The down pass's tall tiles (a group of more than 32 rows in a
+// decode-sized batch, listed once with the fourth descriptor field 1) run
+// with eight row blocks, so a hot expert's down weights are streamed once
+// per 128 rows instead of once per 32; every other tile, and every gate/up
+// tile, with two.  (Gate/up keeps 32-row tiles: its eight-row-block items
+// carry four times the MFMAs, scalings and fragment reads of a K block and
+// were slower than the repeated stream.)
+static constexpr int kWsRows = 2, kWsTallRows = 8;
+
+template <int MODE>
+__global__ __launch_bounds__(512) void k_wstream_fp8(K8Args a) {
+  constexpr int NMAX = MODE == M8_DOWN ? kWsTallRows : kWsRows;
+  constexpr int NS = ((16 * NMAX + 63) / 64 + 1) * 64;   // scale slices + dump
+  __shared__ u32x4_t la0[NMAX * 128], la1[NMAX * 128], la2[NMAX * 128],
+      la3[NMAX * 128];
+  __shared__ __attribute__((aligned(16))) float ls0[NS], ls1[NS], ls2[NS], ls3[NS];
+  const int total = a.tile_count[0] * a.nb_per_tile;
+  // As many workgroups as make the rounds of the persistent loop equal (a
+  // multiple of 8 for the XCD mapping); the rest exit at once.  A short last
+  // round leaves the weight stream to a fraction of the CUs (low-latency
+  // layer -2 %).
+  const int rounds = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int G = min((int)gridDim.x, (((total + rounds - 1) / max(rounds, 1)) + 7) & ~7);
+  const int per_xcd = G >> 3;
+  if ((int)blockIdx.x >= G) return;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  for (int base = 0; base < total; base += G) {
+    const int item = base + xcd * per_xcd + slot;
+    if (item >= total) continue;                 // uniform for the workgroup
+    const int tile = item / a.nb_per_tile;
+    const int nb = item - tile * a.nb_per_tile;
+    const int4 td = a.tiles[tile];
+    if (MODE == M8_DOWN && td.w)
+      wstream_item<MODE, kWsTallRows>(a, td, nb, la0, la1, la2, la3, ls0, ls1, ls2, ls3);
+    else
+      wstream_item<MODE, kWsRows>(a, td, nb, la0, la1, la2, la3, ls0, ls1, ls2, ls3);
   }
 }
 
@@ -852,6 +883,12 @@ __global__ __launch_bounds__(256) void k_quant_h_fp8(
 // to 160 rows), both balanced; else the 128 x 128 tiled kernel.  Both
 // streaming kernels' down pass covers 256 channels an item, so they need
 // H % 256 == 0.
+// The FP8 streaming recipe's down pass runs a group of more than 32 rows in
+// tall tiles of up to 128 rows, listed once, from a list of its own.
+int ffn_down_tall_rows(int wdt, int BM) {
+  return (wdt == MOE_FP8_E4M3 && BM == 32) ? -128 : 0;
+}
+
 int ffn_fp8_tile_rows(int rows_hint, int H, int I, int* balanced) {
   (void)I;
   *balanced = 0;
@@ -864,7 +901,7 @@ template <int MODE>
 static void launch_stream_fp8(const K8Args& a, int BM, hipStream_t s) {
   // one workgroup per CU (LDS); a multiple of 8 for the XCD-major order
   if (BM == 32)
-    k_wstream_fp8<MODE, 2><<<256, 512, 0, s>>>(a);
+    k_wstream_fp8<MODE><<<256, 512, 0, s>>>(a);
   else
     k_ring_fp8<MODE, 10><<<256, 512, 0, s>>>(a);
 }
@@ -877,7 +914,9 @@ hipError_t launch_ffn_fp8(FfnArgs& f, hipStream_t s) {
   const bool stream = balanced != 0;
   if (!f.tiles_ready)
     launch_build_tiles(f.offsets, f.P, f.has_shared, f.T, BM, balanced, 0,
-                       f.tiles, f.tile_count, s);
+                       f.tiles, f.tile_count, ffn_down_tall_rows(f.wdt, BM),
+                       ffn_down_tall_rows(f.wdt, BM) ? f.tiles_down : nullptr,
+                       f.tile_count + 1, s);
   if (f.events) hipEventRecord(f.events[0], s);
   const long hrows = (long)f.cap + (f.has_shared ? f.T : 0);
   const long max_tiles = G + hrows / BM + 1;
@@ -950,6 +989,10 @@ hipError_t launch_ffn_fp8(FfnArgs& f, hipStream_t s) {
   a.s1_sh = nullptr;
   a.y_routed = f.y_routed;
   a.y_shared = f.y_shared;
+  if (ffn_down_tall_rows(f.wdt, BM)) {     // down's own list (tall tiles)
+    a.tiles = f.tiles_down;
+    a.tile_count = f.tile_count + 1;
+  }
   a.nb_per_tile = a.N / (stream ? 256 : 128);
   items = max_tiles * a.nb_per_tile;
   grid = items < cu * 2 ? items : cu * 2;
