@@ -119,12 +119,18 @@ COUNTERS = {
         "write_kib": 33232.1, "write_factor": 1.0,
         "mfma_util": 0.295},
     "lowlat": {
-        "kernel": "k_wstream_fp8<0, 2>", "profile": "profiles/layer_wstream_fp8_lowlat.md",
+        "kernel": "k_wstream_fp8<0>", "profile": "profiles/layer_wstream_fp8_lowlat.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn_fp8.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "997ca6fdc9b5006f",
-        "fetch_kib": 452611.3, "fetch_factor": 1.9594,
+        "sha": "445bfbd4fb0ec97e",
+        "fetch_kib": 452572.8, "fetch_factor": 1.9637,
         "write_kib": 278.1, "write_factor": 1.0,
-        "mfma_util": 0.079},
+        "mfma_util": 0.080},
+    "lowlat_skewed": {
+        "kernel": "k_wstream_fp8<0>", "profile": "profiles/layer_wstream_fp8_lowlat_skewed.md",
+        "files": ["expert_moe_fp32_amd/csrc/ffn_fp8.hip", "expert_moe_fp32_amd/csrc/common.h"],
+        "sha": "445bfbd4fb0ec97e",
+        "fetch_kib": 162262.5, "fetch_factor": 1.9637,
+        "write_kib": 566.7, "write_factor": 1.0},
 }
 
 
