@@ -42,7 +42,8 @@
 
 namespace moe {
 
-enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
+// MODE_DOWN3: the streaming kernel's down pass with three blocks a wavefront
+enum { MODE_GATEUP = 0, MODE_DOWN = 1, MODE_DOWN3 = 2 };
 
 struct KArgs {
   const int4* tiles;
@@ -147,27 +148,32 @@ __device__ __forceinline__ void store_block(const KArgs& a, bool sh, int row0,
 }
 
 // ---------------------------------------------- weight-streaming kernel
-// Workgroup = 4 wavefronts; wavefront w streams two packed row blocks (16
+// Workgroup = 4 wavefronts; wavefront w streams packed row blocks (16
 // channels each) over the whole reduction: gate and up of block nb*4 + w
-// (64 outputs an item), or the neighbouring down blocks nb*8 + 2w and
-// nb*8 + 2w + 1 (128 outputs an item; adjacent runs, and each row's two
-// 16-float output blocks fill one 128-byte line -- the decode down pass ran
-// 138 -> 133 us against blocks 64 channels apart), so every wavefront keeps
-// two weight streams in flight.
+// (64 outputs an item), or NBW neighbouring down blocks from nb*4*NBW +
+// NBW*w (adjacent runs, and each row's 16-float output blocks fill whole
+// 128-byte lines -- the decode down pass ran 138 -> 133 us with two blocks
+// against blocks 64 channels apart).  Down takes three blocks a wavefront
+// (MODE_DOWN3, 192 outputs an item) when H is a multiple of 192, else two:
+// three weight streams in flight per wavefront and 2 instead of 3 rounds of
+// items at the decode shape ran down 133 -> 129 us.
 // A tile has up to 16*NMB rows.  K chunk = 128 (4 MFMA steps), prefetched
 // one chunk ahead.
 //
 // A group larger than one tile (a hot expert in a decode batch) is cut into
 // tall tiles of up to 4 * 16 * NMB rows instead, each listed four times
 // (descriptor mark 1 + Q, Q = 0..3): item (quarter Q, nb) has all four
-// wavefronts stream the same two weight columns -- gate and up of block
-// nb*4 + Q, or down blocks nb*8 + 2Q and nb*8 + 2Q + 1 -- each for its own 16
+// wavefronts stream the same weight columns -- gate and up of block nb*4 + Q,
+// or down blocks nb*4*NBW + NBW*Q onwards -- each for its own 16
 // * NMB rows of the tile.  The four identical streams go through the caches
 // (ordinary loads: the first miss fetches, the others hit), so a hot
 // expert's weights come from memory once per tall tile rather than once per
 // 16 * NMB rows; small tiles keep the non-temporal stream.
 template <int MODE, int NMB>
 __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
+  constexpr bool DOWN = MODE != MODE_GATEUP;
+  constexpr int NBW = MODE == MODE_DOWN3 ? 3 : 2;   // down blocks a wavefront
+  constexpr int SM = DOWN ? MODE_DOWN : MODE_GATEUP;  // store_block's mode
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c16 = lane & 15, q = lane >> 4;
   const int total = a.tile_count[0] * a.nb_per_tile;
@@ -182,7 +188,7 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
     const int wcol = quarter ? quarter - 1 : wv; // the wave's column block
     const int wrow = quarter ? 16 * NMB * wv : 0;  // and first tile row
     const int row0 = td.y + wrow, nrows = td.z - wrow;   // this wave's rows
-    const int nb16 = MODE == MODE_GATEUP ? nb * 4 + wcol : nb * 8 + 2 * wcol;
+    const int nb16 = MODE == MODE_GATEUP ? nb * 4 + wcol : nb * (4 * NBW) + NBW * wcol;
     const u32x4_t* b0p = (const u32x4_t*)(sh ? a.w0_sh : a.w0_arr[g]) +
                          (size_t)nb16 * KB * 64 + lane;
     const u32x4_t* b1p =
@@ -199,11 +205,13 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
     }
     // active row blocks of this wave (uniform; none past a tall tile's end)
     const int nmb = nrows <= 0 ? 0 : min((nrows + 15) >> 4, NMB);
-    f32x4_t acc0[NMB], acc1[NMB];
+    const u32x4_t* b2p = b1p + (size_t)KB * 64;    // MODE_DOWN3's third block
+    f32x4_t acc0[NMB], acc1[NMB], acc2[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       acc0[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       acc1[mb] = acc0[mb];
+      acc2[mb] = acc0[mb];
     }
     const u32x4_t zero = {0u, 0u, 0u, 0u};
     // A quarter wavefront without rows streams nothing but keeps the
@@ -215,17 +223,18 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
       auto wload = [&](const u32x4_t* p) -> u32x4_t {
         return NT ? load_nt(p) : (active ? *p : zero);
       };
-      u32x4_t b0c[4], b1c[4], acur[NMB][4];
+      u32x4_t b0c[4], b1c[4], b2c[4], acur[NMB][4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         b0c[s] = wload(b0p + s * 64);
         b1c[s] = wload(b1p + s * 64);
+        if (NBW == 3) b2c[s] = wload(b2p + s * 64);
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
           acur[mb][s] = av[mb] ? *(const u32x4_t*)(ap[mb] + 32 * s) : zero;
       }
       for (int k0 = 0; k0 < K; k0 += 128) {
-        u32x4_t b0n[4], b1n[4], anext[NMB][4];
+        u32x4_t b0n[4], b1n[4], b2n[4], anext[NMB][4];
         const bool more = k0 + 128 < K;
         if (!NT) __syncthreads();                // the quarter's four streams
         if (more) {
@@ -234,6 +243,7 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
           for (int s = 0; s < 4; ++s) {
             b0n[s] = wload(b0p + (kb + s) * 64);
             b1n[s] = wload(b1p + (kb + s) * 64);
+            if (NBW == 3) b2n[s] = wload(b2p + (kb + s) * 64);
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
               anext[mb][s] = av[mb] ? *(const u32x4_t*)(ap[mb] + k0 + 128 + 32 * s) : zero;
@@ -246,6 +256,7 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
             if (mb < nmb) {
               acc0[mb] = mfma16(acur[mb][s], b0c[s], acc0[mb]);
               acc1[mb] = mfma16(acur[mb][s], b1c[s], acc1[mb]);
+              if (NBW == 3) acc2[mb] = mfma16(acur[mb][s], b2c[s], acc2[mb]);
             }
           }
         }
@@ -254,6 +265,7 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
           for (int s = 0; s < 4; ++s) {
             b0c[s] = b0n[s];
             b1c[s] = b1n[s];
+            if (NBW == 3) b2c[s] = b2n[s];
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) acur[mb][s] = anext[mb][s];
           }
@@ -266,9 +278,11 @@ __global__ __launch_bounds__(256) void k_stream_bf16(KArgs a) {
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       if (mb >= nmb) continue;
-      store_block<MODE>(a, sh, row0, nrows, mb * 16, n, acc0[mb], acc1[mb]);
-      if (MODE == MODE_DOWN)
-        store_block<MODE>(a, sh, row0, nrows, mb * 16, n + 16, acc1[mb], acc1[mb]);
+      store_block<SM>(a, sh, row0, nrows, mb * 16, n, acc0[mb], acc1[mb]);
+      if (DOWN)
+        store_block<SM>(a, sh, row0, nrows, mb * 16, n + 16, acc1[mb], acc1[mb]);
+      if (NBW == 3)
+        store_block<SM>(a, sh, row0, nrows, mb * 16, n + 32, acc2[mb], acc2[mb]);
     }
   }
 }
@@ -629,11 +643,13 @@ hipError_t launch_ffn(FfnArgs& f, hipStream_t s) {
     long grid = items < cu * 4 ? items : cu * 4;
     k_f32<MODE_DOWN><<<(unsigned)grid, 256, 0, s>>>(a);
   } else if (stream) {
-    a.nb_per_tile = a.N / 128;                // two neighbouring blocks per wave
+    const bool three = a.N % 192 == 0;       // three neighbouring blocks a wave
+    a.nb_per_tile = a.N / (three ? 192 : 128);
     long items = max_tiles * a.nb_per_tile;
     // persistent: the two workgroups a CU holds at this kernel's registers
     long grid = items < cu * 2 ? items : cu * 2;
-    k_stream_bf16<MODE_DOWN, 2><<<(unsigned)grid, 256, 0, s>>>(a);
+    if (three) k_stream_bf16<MODE_DOWN3, 2><<<(unsigned)grid, 256, 0, s>>>(a);
+    else k_stream_bf16<MODE_DOWN, 2><<<(unsigned)grid, 256, 0, s>>>(a);
   } else if (ring && f.H % 256 == 0) {
     hipError_t e = launch_gemm_bf16_down(f, s);
     if (e != hipSuccess) return e;
