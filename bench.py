@@ -80,9 +80,9 @@ COUNTERS = {
         "kernel": "k_stream_bf16<0, 2>", "profile": "profiles/layer_stream_bf16_decode.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
         "sha": "9e1fa603705553fa",
-        "fetch_kib": 794476.7, "fetch_factor": 1.9976,
+        "fetch_kib": 794472.6, "fetch_factor": 1.9976,
         "write_kib": 988.7, "write_factor": 1.0,
-        "mfma_util": 0.052},
+        "mfma_util": 0.051},
     "decode_skewed": {
         "kernel": "k_stream_bf16<0, 2>", "profile": "profiles/layer_stream_bf16_decode_skewed.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
