@@ -114,21 +114,21 @@ COUNTERS = {
     "fp8": {
         "kernel": "k_ring_fp8<0, 10>", "profile": "profiles/layer_ring_fp8_fp8.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn_fp8.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "445bfbd4fb0ec97e",
+        "sha": "74796710a92125a6",
         "fetch_kib": 485368.9, "fetch_factor": 1.9987,
         "write_kib": 33232.1, "write_factor": 1.0,
         "mfma_util": 0.295},
     "lowlat": {
         "kernel": "k_wstream_fp8<0>", "profile": "profiles/layer_wstream_fp8_lowlat.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn_fp8.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "445bfbd4fb0ec97e",
+        "sha": "74796710a92125a6",
         "fetch_kib": 452572.8, "fetch_factor": 1.9637,
         "write_kib": 278.1, "write_factor": 1.0,
         "mfma_util": 0.080},
     "lowlat_skewed": {
         "kernel": "k_wstream_fp8<0>", "profile": "profiles/layer_wstream_fp8_lowlat_skewed.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn_fp8.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "445bfbd4fb0ec97e",
+        "sha": "74796710a92125a6",
         "fetch_kib": 162262.5, "fetch_factor": 1.9637,
         "write_kib": 566.7, "write_factor": 1.0},
 }

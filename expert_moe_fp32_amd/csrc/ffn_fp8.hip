@@ -877,17 +877,18 @@ __global__ __launch_bounds__(256) void k_quant_h_fp8(
   }
 }
 
-// Tile rows of the FP8 recipe for an expected group size: the
-// register weight-streaming kernel with 32-row tiles (a few rows per
-// expert) or the LDS-ring kernel with 160-row tiles (one tile per expert up
-// to 160 rows), both balanced; else the 128 x 128 tiled kernel.  Both
-// streaming kernels' down pass covers 256 channels an item, so they need
-// H % 256 == 0.
 // The FP8 streaming recipe's down pass runs a group of more than 32 rows in
 // tall tiles of up to 128 rows, listed once, from a list of its own.
 int ffn_down_tall_rows(int wdt, int BM) {
   return (wdt == MOE_FP8_E4M3 && BM == 32) ? -128 : 0;
 }
+
+// Tile rows of the FP8 recipe for an expected group size: the
+// register weight-streaming kernel with 32-row tiles (a few rows per
+// expert; the down pass puts a larger group in tall tiles) or the LDS-ring
+// kernel with 160-row tiles (one tile per expert up to 160 rows), both
+// balanced; else the 128 x 128 tiled kernel.  Both streaming kernels' down
+// pass covers 256 channels an item, so they need H % 256 == 0.
 
 int ffn_fp8_tile_rows(int rows_hint, int H, int I, int* balanced) {
   (void)I;
