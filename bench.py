@@ -73,20 +73,20 @@ COUNTERS = {
     "tiny": {
         "kernel": "k_f32<0>", "profile": "profiles/layer_f32_tiny.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "9e1fa603705553fa",
+        "sha": "a61869c6790dad6e",
         "fetch_kib": 1831.6, "fetch_factor": 1.5784,
         "write_kib": 128.0, "write_factor": 1.0},
     "decode": {
         "kernel": "k_stream_bf16<0, 2>", "profile": "profiles/layer_stream_bf16_decode.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "9e1fa603705553fa",
+        "sha": "a61869c6790dad6e",
         "fetch_kib": 794472.6, "fetch_factor": 1.9976,
         "write_kib": 988.7, "write_factor": 1.0,
         "mfma_util": 0.051},
     "decode_skewed": {
         "kernel": "k_stream_bf16<0, 2>", "profile": "profiles/layer_stream_bf16_decode_skewed.md",
         "files": ["expert_moe_fp32_amd/csrc/ffn.hip", "expert_moe_fp32_amd/csrc/common.h"],
-        "sha": "9e1fa603705553fa",
+        "sha": "a61869c6790dad6e",
         "fetch_kib": 207722.8, "fetch_factor": 1.9976,
         "write_kib": 875.4, "write_factor": 1.0,
         "mfma_util": 0.052},

@@ -20,10 +20,11 @@
 // contiguous run.
 //
 // bf16 kernels on the tile list:
-//  * k_stream_bf16 (groups of a few rows, decode): each wavefront streams its
-//    16 output channels' contiguous run straight into MFMA operand registers
-//    with non-temporal loads, one 128-wide K chunk ahead; every weight byte
-//    is read once per tile.
+//  * k_stream_bf16 (groups of a few rows, decode): each wavefront streams
+//    contiguous runs of 16 output channels (gate and up, or two to three
+//    down blocks) straight into MFMA operand registers with non-temporal
+//    loads, one 128-wide K chunk ahead; every weight byte is read once per
+//    tile.
 //  * k_gemm_bf16 (gemm_bf16.hip; groups of hundreds of rows, prefill): the
 //    256 x 256 LDS-ring GEMM for gate/up and down.
 //  * k_tile_bf16_down: 128 rows x 128 columns per workgroup, double-buffered LDS
